@@ -1,0 +1,92 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must make at
+least one pin fail, or the pins would not be worth trusting."""
+
+import numpy as np
+import pytest
+
+import test_oracle_attention as ta
+import test_oracle_codec as tc
+from oracle import attention, codec
+from oracle_pins import parse_worked_examples
+
+_orig_encode = codec.encode_blocks
+_orig_attend = attention.attend
+
+
+def _swap_nibbles(x, fmt):
+    out = _orig_encode(x, fmt)
+    if fmt == "q4":
+        out[..., 2:] = ((out[..., 2:] & 0x0F) << 4) | (out[..., 2:] >> 4)
+    return out
+
+
+def _big_endian_scale(x, fmt):
+    out = _orig_encode(x, fmt)
+    out[..., [0, 1]] = out[..., [1, 0]]
+    return out
+
+
+def _quantize_with_stored_scale(x, fmt):
+    # quantizes with the fp16 scale d instead of the binary32 scale s
+    qm = np.float32(codec.qmax(fmt))
+    xf = x.astype(np.float32)
+    amax = np.abs(xf).max(axis=-1)
+    d = (amax / qm).astype(np.float16)
+    ds = np.where(d > 0, d.astype(np.float32), np.float32(1))
+    q = np.clip(np.rint(xf / ds[..., None]), -qm, qm)
+    q = np.where((d > 0)[..., None], q, 0).astype(np.int8)
+    out = _orig_encode(x, fmt)
+    qb = q.view(np.uint8)
+    out[..., 2:] = qb if fmt == "q8" else (qb[..., 0::2] & 0xF) | ((qb[..., 1::2] & 0xF) << 4)
+    return out
+
+
+def _round_half_up(monkeypatch):
+    floor = np.floor
+    monkeypatch.setattr(np, "rint", lambda a: floor(np.asarray(a) + np.float32(0.5)))
+
+
+def _codec_pins():
+    for ex in parse_worked_examples():
+        tc.test_worked_examples_encode(ex)
+    tc.test_codec_invariants("q8")
+    tc.test_codec_invariants("q4")
+
+
+@pytest.mark.parametrize("mutant", [_swap_nibbles, _big_endian_scale, _quantize_with_stored_scale])
+def test_codec_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(codec, "encode_blocks", mutant)
+    with pytest.raises(AssertionError):
+        _codec_pins()
+
+
+def test_round_half_up_is_caught(monkeypatch):
+    _round_half_up(monkeypatch)
+    with pytest.raises(AssertionError):
+        _codec_pins()
+
+
+def _sees_one_future_key(q, k, v, positions, sm_scale):
+    return _orig_attend(q, k, v, np.minimum(np.asarray(positions) + 1, k.shape[0] - 1), sm_scale)
+
+
+def _wrong_group_mapping(q, k, v, positions, sm_scale):
+    return _orig_attend(q, k[:, ::-1], v[:, ::-1], positions, sm_scale)
+
+
+def _keys_and_values_swapped(q, k, v, positions, sm_scale):
+    return _orig_attend(q, v, k, positions, sm_scale)
+
+
+def _scale_dropped(q, k, v, positions, sm_scale):
+    return _orig_attend(q, k, v, positions, 1.0)
+
+
+@pytest.mark.parametrize("mutant", [_sees_one_future_key, _wrong_group_mapping,
+                                    _keys_and_values_swapped, _scale_dropped])
+def test_attention_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(attention, "attend", mutant)
+    with pytest.raises(AssertionError):
+        ta.test_brute_force_tiny("q8", "q4")
+    with pytest.raises(AssertionError):
+        ta.test_codec_free_case_matches_torch_sdpa()
