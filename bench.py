@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-batch quantized-KV attention step on one MI355X.
+
+A step is one pass of the whole hot path over the workload's batch:
+kv_append_quant of the step's new K/V rows, then mixed_attention_fwd over the
+paged cache (every layer, for the multi-layer workload).  Inputs are resident
+in HBM before timing; the cached prefix is written beforehand by the same
+append kernel.  To keep the Infinity Cache from serving repeated reads of a
+working set near its 256 MB size, the timed steps rotate over several
+identical copies of the pools (enough copies to exceed 1 GiB).
+
+Prints one JSON line.  ``value`` is the effective KV bandwidth of the step:
+the bytes of every visible cached position (prefix and new rows, K and V, in
+their block format) read once per KV head, divided by the step time.  The
+attention launches are timed separately with HIP events on the stream they
+run on, for the roofline figure.  The oracle is timed on the host on a bounded
+sample of the same workload for the cpu_baseline figure.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mixed-batch quantized-KV attention: effective KV GB/s and query tok/s per step"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "decode16": "16 decode rows, 24 q heads / 4 KV heads, head_dim 128, q8 34-byte blocks, "
+                "page 256, contexts uniform in [1024, 32768], 2% K outlier channels x20, 1 layer",
+    "mixed16_chunk2k": "16 decode rows (contexts uniform in [2048, 65536]) + one 2048-row chunk at "
+                       "position 131072, 24/4 heads, head_dim 128, q8, page 256, K outliers, 1 layer",
+    "long_q8": "one decode row at context 262144, 24/4 heads, head_dim 128, q8, page 256, 1 layer",
+    "long_k4v4": "one decode row at context 262144, 24/4 heads, head_dim 128, K4V4 18-byte blocks, "
+                 "page 256, 1 layer",
+    "step_k4v4": "12 attention layers, each: 16 decode rows (contexts log-uniform in [512, 262144]) + "
+                 "a 2048-row chunk at 131072, 24/4 heads, head_dim 128, K4V4, page 256, K outliers",
+}
+SEEDS = {"decode16": 2, "mixed16_chunk2k": 3, "long_q8": 4, "long_k4v4": 4, "step_k4v4": 5}
+
+
+def kv_bytes_per_position(layout):
+    from mixed_attention_block_amd import kv_block_bytes
+    nb = layout["head_dim"] // 32
+    return layout["num_kv_heads"] * nb * (kv_block_bytes(layout["k_format"]) +
+                                          kv_block_bytes(layout["v_format"]))
+
+
+def chunk_flops(case):
+    """QK^T and PV flops of the chunk rows over their visible keys (unmasked pairs)."""
+    lay = case.layout
+    f = 0
+    for s in range(case.num_seqs):
+        n = case.q_len(s)
+        if n > 1:
+            p = int(case.prefix_len[s])
+            f += 4 * lay["head_dim"] * lay["num_q_heads"] * (n * (p + 1) + n * (n - 1) // 2)
+    return f
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The oracle on whole sequences of the case, in order, until the budget is spent."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+
+    lay = case.layout
+    bpp = kv_bytes_per_position(lay)
+    kp = ocache.new_pool(lay, lay["k_format"])
+    vp = ocache.new_pool(lay, lay["v_format"])
+    order = sorted(range(case.num_seqs), key=lambda s: case.context(s))  # short first
+    done, nbytes, rows, elapsed = [], 0, 0, 0.0
+    for s in order:
+        r0, r1 = int(case.q_start[s]), int(case.q_start[s + 1])
+        k = torch.cat([case.k_prefix[s].cpu(), case.k_new[r0:r1].cpu()]).numpy()
+        v = torch.cat([case.v_prefix[s].cpu(), case.v_new[r0:r1].cpu()]).numpy()
+        q = case.q.cpu().numpy()
+        t0 = time.perf_counter()
+        pos = np.arange(case.context(s))
+        ocache.write_tokens(kp, lay, lay["k_format"], case.block_table[s], pos, k)
+        ocache.write_tokens(vp, lay, lay["v_format"], case.block_table[s], pos, v)
+        oattn.attention(q, kp, vp, lay, case.q_start, case.prefix_len, case.block_table,
+                        case.sm_scale, rows=list(range(r0, r1)))
+        elapsed += time.perf_counter() - t0
+        done.append(s)
+        nbytes += case.context(s) * bpp
+        rows += r1 - r0
+        if elapsed >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {case.num_seqs} sequences of this workload (shortest first; "
+                      f"{rows} rows, {nbytes / 1e6:.1f} MB of KV): encode + fp64 attention, "
+                      f"{elapsed:.1f} s",
+            "query_tok_s": round(rows / elapsed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode16", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="pool copies rotated (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; runs on more than one GPU are not "
+              "part of it (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixed_attention_block_amd as mab
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_harness import GpuState
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    layers = 12 if name == "step_k4v4" else 1
+    seed = SEEDS[name]
+
+    # ---- set-up (untimed): cases, pools, prefix fill, pool copies -----------------
+    states = []
+    kv_bytes = 0
+    rows = 0
+    flops = 0
+    first_case = None
+    for layer in range(layers):
+        case = synth.make_case(name, seed, device="cuda",
+                               value_seed=seed * 100 + layer if layers > 1 else None)
+        st = GpuState(case)
+        st.append_step()
+        bpp = kv_bytes_per_position(case.layout)
+        kv_bytes += sum(case.context(s) for s in range(case.num_seqs)) * bpp
+        rows = case.num_rows  # the layers share one batch
+        flops += chunk_flops(case)
+        st.q = case.q.contiguous()
+        st.k_new = case.k_new.contiguous()
+        st.v_new = case.v_new.contiguous()
+        st.ws = st.workspace()
+        st.out = torch.empty((case.num_rows, case.layout["num_q_heads"], case.layout["head_dim"]),
+                             dtype=torch.float32, device="cuda")
+        if first_case is None:
+            first_case = case
+        else:  # keep only what the timed loop needs
+            case.k_prefix = case.v_prefix = None
+        states.append(st)
+    per_layer_pool = states[0].k_pool.numel() + states[0].v_pool.numel()
+    copies = args.copies or (max(1, min(16, math.ceil((1 << 30) / (per_layer_pool * layers))))
+                             if layers == 1 else 1)
+    pools = [[(st.k_pool, st.v_pool)] for st in states]
+    for i, st in enumerate(states):
+        for _ in range(copies - 1):
+            pools[i].append((st.k_pool.clone(), st.v_pool.clone()))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(it, ev=None):
+        for i, st in enumerate(states):
+            kp, vp = pools[i][it % copies]
+            if ev is not None:
+                ev[0].record(stream)
+            mab.kv_append_quant(st.layout, st.batch, st.k_new, st.v_new, kp, vp, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            mab.mixed_attention_fwd(st.layout, st.batch, st.q, kp, vp, st.case.sm_scale, st.out,
+                                    st.ws, stream)
+            if ev is not None:
+                ev[2].record(stream)
+                ev = ev[3:]
+
+    for it in range(args.warmup):
+        step(it)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps -------------------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * layers)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for it in range(args.steps):
+        step(args.warmup + it, evs[it])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    attn_ms = [e[3 * l + 1].elapsed_time(e[3 * l + 2]) for e in evs for l in range(layers)]
+    app_ms = [e[3 * l].elapsed_time(e[3 * l + 1]) for e in evs for l in range(layers)]
+    attn_avg = float(np.mean(attn_ms))
+    kv_per_launch = kv_bytes / layers
+    achieved = kv_per_launch / (attn_avg * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{name}: {WORKLOADS[name]}",
+            "seed": seed,
+            "layers": layers,
+            "query_rows_per_step": rows,
+            "kv_bytes_per_step": int(kv_bytes),
+            "kv_format": f"K{first_case.layout['k_format']}/V{first_case.layout['v_format']}",
+            "pool_copies_rotated": copies,
+        },
+        "query_tok_s": round(rows / (ms_per_step * 1e-3), 1),
+        "attention_ms_avg": round(attn_avg, 6),
+        "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 6),
+                                 round(float(np.percentile(attn_ms, 90)), 6)],
+        "append_ms_avg": round(float(np.mean(app_ms)), 6),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mixed_attention_fwd (attention_kernel + combine_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if flops:
+        tf = flops / layers / (attn_avg * 1e-3) / 1e12
+        result["chunk_mfma"] = {"flops_per_launch": int(flops / layers), "achieved_tflops": round(tf, 2),
+                                "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                                "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(first_case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

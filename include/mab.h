@@ -1,0 +1,175 @@
+/*
+ * mab.h -- C ABI of the mixed-batch attention library for a paged,
+ * block-quantized KV cache (AMD Instinct MI355X, gfx950).
+ *
+ * Source of the operations: the MBufo page "自研RDNA高併發推論引擎 以AI Max+ 395為範例"
+ * (lcz.me, topic 2938).
+ *   - Section 1 ("高併發（架構差異）"): the rows of one bounded prefill chunk and
+ *     all due single-token decode rows share one ForwardBatch and one attention
+ *     kernel, so the prefill tick also emits every decoder's token.
+ *   - Section 2 ("提供更多壓縮精度（成本差異）"), KV modes table: q8 keeps one f16
+ *     scale per 32 elements (34-byte blocks); the 4-bit modes pack 32 values into
+ *     18-byte blocks; blocked modes are bit-exact at the codec level.
+ *   - Section 2, occupancy table ("佔用"): bytes per position 1088 (q8) and 576
+ *     (K4V4) at 4 KV heads x 128 dims.
+ *
+ * Conventions for every function below:
+ *   - Pointers without a "_host" suffix are DEVICE pointers (HIP device memory
+ *     of the current device); "_host" pointers are host memory read during the
+ *     call only.  The library allocates nothing, keeps no state between calls,
+ *     never synchronizes the stream and never prints, aborts or throws.
+ *   - "stream" is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns at once; results are ready when the stream
+ *     reaches that point.  Calls on one stream run in order.
+ *   - Errors detectable on the host are returned as a non-zero status before
+ *     anything is enqueued (see mab_status_string).  Device arrays must hold
+ *     the same values as their host mirrors; block-table entries must be valid
+ *     page ids in [0, num_pages) for every page a sequence uses.  Violating
+ *     either is undefined behaviour on the device (not detected).
+ *
+ * Data layout (all little-endian, tightly packed, C order):
+ *   block   : 32 consecutive head_dim values of one token and one KV head:
+ *             bytes [0,2) = fp16 scale d; then the codes.
+ *             q8 (34 B): 32 two's-complement int8 codes.
+ *             q4 (18 B): 16 bytes, byte j = code 2j (low nibble) | code 2j+1
+ *                        (high nibble), two's-complement nibbles.
+ *             value = code * d.  Encoding: s = fl32(max|x| / Q) (Q = 127 or 7,
+ *             IEEE binary32 divide), code = clamp(rint_even(fl32(x / s)), -Q, Q),
+ *             d = fp16 round-to-nearest-even of s (no flush); all-zero block:
+ *             d = +0, codes 0.
+ *   pool    : uint8 [num_pages][num_kv_heads][page_size][head_dim/32][B],
+ *             one pool for K (k_format) and one for V (v_format).
+ *   token t of sequence s lives in page block_table[s*max_pages_per_seq + t/page_size],
+ *             slot t % page_size.
+ *   q       : fp16 [num_rows][num_q_heads][head_dim]
+ *   k_new/v_new : fp16 [num_rows][num_kv_heads][head_dim]
+ *   out     : fp32 [num_rows][num_q_heads][head_dim]
+ *   batch   : the rows of sequence s are [q_start[s], q_start[s+1]); row i of s
+ *             sits at position prefix_len[s] + i and attends keys 0 .. that
+ *             position of s (full over the cached prefix, causal inside the
+ *             rows of s).  A decode row is a sequence with one row; its
+ *             context is prefix_len + 1.  Query head h reads KV head
+ *             h / (num_q_heads / num_kv_heads).
+ *
+ * Supported shapes (others return MAB_ERR_UNSUPPORTED or MAB_ERR_SHAPE):
+ *   head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with a group of at
+ *   most 8 query heads per KV head; page_size a positive multiple of 16;
+ *   1 <= rows per sequence; num_seqs <= 4096; all buffers 16-byte aligned.
+ */
+#ifndef MAB_H
+#define MAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  MAB_OK = 0,
+  MAB_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  MAB_ERR_SHAPE = 2,       /* a layout or batch field breaks a stated rule     */
+  MAB_ERR_UNSUPPORTED = 3, /* well-formed but outside the supported shapes     */
+  MAB_ERR_WORKSPACE = 4,   /* workspace smaller than attention_workspace_bytes */
+  MAB_ERR_ALIGN = 5,       /* a device buffer is not 16-byte aligned           */
+  MAB_ERR_HIP = 6          /* the HIP runtime refused a kernel launch          */
+};
+
+/* KV block formats (MBufo page, section 2 modes table). */
+enum {
+  MAB_KV_Q8 = 1, /* 34-byte block: fp16 scale + 32 x int8            */
+  MAB_KV_Q4 = 2  /* 18-byte block: fp16 scale + 16 bytes of 32 x int4 */
+};
+
+/* Shape of the cache and of the attention heads. */
+typedef struct mab_kv_layout {
+  int32_t num_q_heads;  /* Hq                                    */
+  int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0                    */
+  int32_t head_dim;     /* D                                     */
+  int32_t page_size;    /* tokens per page                       */
+  int32_t num_pages;    /* pages in each pool                    */
+  int32_t k_format;     /* MAB_KV_Q8 or MAB_KV_Q4                */
+  int32_t v_format;     /* MAB_KV_Q8 or MAB_KV_Q4                */
+  int32_t reserved;     /* must be 0                             */
+} mab_kv_layout;
+
+/* One ForwardBatch: chunk rows and decode rows together (MBufo page, section 1). */
+typedef struct mab_batch {
+  int32_t num_seqs;          /* S                                                 */
+  int32_t num_rows;          /* total query rows = q_start[S]                     */
+  int32_t max_pages_per_seq; /* row stride of block_table                         */
+  int32_t reserved;          /* must be 0                                         */
+  const int32_t* q_start;         /* device [S+1], q_start[0] = 0, non-decreasing */
+  const int32_t* prefix_len;      /* device [S], cached positions before the rows */
+  const int32_t* block_table;     /* device [S * max_pages_per_seq] page ids      */
+  const int32_t* q_start_host;    /* host mirror of q_start                       */
+  const int32_t* prefix_len_host; /* host mirror of prefix_len                    */
+} mab_batch;
+
+/* Bytes of one 32-value block of `format` (34 or 18); 0 for an unknown format. */
+int32_t kv_block_bytes(int32_t format);
+
+/* Bytes of one pool of `format` for `layout`:
+ * num_pages * num_kv_heads * page_size * (head_dim/32) * kv_block_bytes(format).
+ * Returns -1 if the layout is invalid. */
+int64_t kv_pool_bytes(const mab_kv_layout* layout, int32_t format);
+
+/* Device workspace that mixed_attention_fwd needs for this batch (split-K
+ * partial results and small per-row tables).  Computed from the host mirrors.
+ * Returns a negative status (-MAB_ERR_*) if the layout or batch is invalid. */
+int64_t attention_workspace_bytes(const mab_kv_layout* layout, const mab_batch* batch);
+
+/* kv_append_quant: quantize the step's new keys and values into the cache.
+ *
+ * Operation (MBufo page, section 2 modes table, codec as in the header
+ * comment): for every row i of sequence s, every KV head g and every 32-value
+ * block b, encode k_new[row][g][32b .. 32b+31] into the k_format block at
+ * position prefix_len[s] + i of sequence s, and likewise v_new into the
+ * v_format pool.  Bytes written are bit-identical to the stated encoding.
+ * Only the blocks of the batch's rows are written; nothing else in the pools
+ * changes.  Call it before mixed_attention_fwd in the same step: attention
+ * reads every key, the rows' own included, from the cache.
+ *
+ * k_new, v_new : device fp16 [num_rows][Hkv][D], read only.
+ * k_pool, v_pool : device pools (layout above), written in place.
+ * Rows of one call must not target the same position twice. */
+int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch,
+                        const void* k_new, const void* v_new,
+                        void* k_pool, void* v_pool, void* stream);
+
+/* mixed_attention_fwd: one attention step of a mixed batch over the cache.
+ *
+ * Operation (MBufo page, section 1: chunk and decode rows in one ForwardBatch
+ * and one attention kernel): for each row r of sequence s at position
+ * t = prefix_len[s] + (r - q_start[s]) and each query head h with KV head
+ * g = h / (Hq/Hkv),
+ *     z_j = sm_scale * <q[r][h], K_hat[s][j][g]>,  j = 0 .. t
+ *     out[r][h] = sum_j softmax(z)_j * V_hat[s][j][g]
+ * where K_hat, V_hat are the dequantized cache blocks.  Arithmetic: fp16
+ * operands on the matrix cores with fp32 accumulation, fp32 online softmax,
+ * split-K over key ranges merged by log-sum-exp in fixed order.  The result
+ * is deterministic and independent of the physical page ids and of which
+ * other sequences share the batch.
+ *
+ * q          : device fp16 [num_rows][Hq][D], read only.
+ * k_pool, v_pool : device pools, read only.
+ * sm_scale   : softmax scale (typically 1/sqrt(D)).
+ * out        : device fp32 [num_rows][Hq][D], fully written.
+ * workspace  : device scratch of at least attention_workspace_bytes() bytes,
+ *              owned by the caller; contents need not be initialized and are
+ *              clobbered.  Concurrent calls need distinct workspaces. */
+int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
+                            const void* q, const void* k_pool, const void* v_pool,
+                            float sm_scale, float* out,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* mab_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAB_H */

@@ -1,0 +1,163 @@
+"""Python binding of the mixed-batch quantized-KV attention library (libmab.so).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI declared in ``include/mab.h``.  PyTorch provides
+device memory and the current stream; nothing here computes on tensors.  The
+functions carry the names of the C entry points.
+
+If the shared library has not been built, every call raises ``RuntimeError``
+(build it with ``python -m mixed_attention_block_amd.build``); there is no
+fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmab.so")
+
+MAB_KV_Q8 = 1
+MAB_KV_Q4 = 2
+FORMATS = {"q8": MAB_KV_Q8, "q4": MAB_KV_Q4}
+
+
+class MabError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {mab_status_string(status)}")
+
+
+class KVLayout(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("k_format", ctypes.c_int32),
+                ("v_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_start", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("q_start_host", ctypes.c_void_p),
+                ("prefix_len_host", ctypes.c_void_p)]
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixed_attention_block_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        lay, bat = ctypes.POINTER(KVLayout), ctypes.POINTER(Batch)
+        lib.kv_block_bytes.argtypes, lib.kv_block_bytes.restype = [i32], i32
+        lib.kv_pool_bytes.argtypes, lib.kv_pool_bytes.restype = [lay, i32], i64
+        lib.attention_workspace_bytes.argtypes = [lay, bat]
+        lib.attention_workspace_bytes.restype = i64
+        lib.kv_append_quant.argtypes = [lay, bat, P, P, P, P, P]
+        lib.kv_append_quant.restype = i32
+        lib.mixed_attention_fwd.argtypes = [lay, bat, P, P, P, f32, P, P, i64, P]
+        lib.mixed_attention_fwd.restype = i32
+        lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
+        _lib_handle = lib
+    return _lib_handle
+
+
+def make_layout(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, k_format="q8",
+                v_format="q8"):
+    """A ``KVLayout``; formats are "q8"/"q4" or the MAB_KV_* integers."""
+    kf = FORMATS.get(k_format, k_format)
+    vf = FORMATS.get(v_format, v_format)
+    return KVLayout(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kf, vf, 0)
+
+
+class BatchDesc:
+    """A ``Batch`` plus the objects whose memory it points to (kept alive here).
+
+    ``q_start``, ``prefix_len``, ``block_table``: int32 device tensors;
+    ``q_start_host``, ``prefix_len_host``: int32 host arrays with the same values.
+    """
+
+    def __init__(self, q_start, prefix_len, block_table, q_start_host, prefix_len_host):
+        self._keep = [q_start, prefix_len, block_table,
+                      np.ascontiguousarray(q_start_host, dtype=np.int32),
+                      np.ascontiguousarray(prefix_len_host, dtype=np.int32)]
+        for t in (q_start, prefix_len, block_table):
+            _check_tensor(t, "int32", "descriptor")
+        qh, ph = self._keep[3], self._keep[4]
+        num_seqs = len(ph)
+        if len(qh) != num_seqs + 1:
+            raise ValueError("q_start_host must have num_seqs + 1 entries")
+        max_pages = block_table.shape[-1] if block_table.dim() == 2 else max(1, block_table.numel())
+        self.struct = Batch(num_seqs, int(qh[-1]) if num_seqs else 0, int(max_pages), 0,
+                            q_start.data_ptr(), prefix_len.data_ptr(), block_table.data_ptr(),
+                            qh.ctypes.data, ph.ctypes.data)
+
+
+def _check_tensor(t, dtype, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if str(t.dtype).split(".")[-1] != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor")
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kv_block_bytes(fmt):
+    return _lib().kv_block_bytes(FORMATS.get(fmt, fmt))
+
+
+def kv_pool_bytes(layout, fmt):
+    return _lib().kv_pool_bytes(ctypes.byref(layout), FORMATS.get(fmt, fmt))
+
+
+def attention_workspace_bytes(layout, batch):
+    n = _lib().attention_workspace_bytes(ctypes.byref(layout), ctypes.byref(batch.struct))
+    if n < 0:
+        raise MabError(-n, "attention_workspace_bytes")
+    return n
+
+
+def kv_append_quant(layout, batch, k_new, v_new, k_pool, v_pool, stream=None):
+    """Quantize the rows' new K/V into the pools (device tensors, in place)."""
+    _check_tensor(k_new, "float16", "k_new")
+    _check_tensor(v_new, "float16", "v_new")
+    _check_tensor(k_pool, "uint8", "k_pool")
+    _check_tensor(v_pool, "uint8", "v_pool")
+    st = _lib().kv_append_quant(ctypes.byref(layout), ctypes.byref(batch.struct),
+                                k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                                v_pool.data_ptr(), _stream_handle(stream))
+    if st:
+        raise MabError(st, "kv_append_quant")
+
+
+def mixed_attention_fwd(layout, batch, q, k_pool, v_pool, sm_scale, out, workspace, stream=None):
+    """One attention step of the mixed batch; writes ``out`` (fp32)."""
+    _check_tensor(q, "float16", "q")
+    _check_tensor(k_pool, "uint8", "k_pool")
+    _check_tensor(v_pool, "uint8", "v_pool")
+    _check_tensor(out, "float32", "out")
+    _check_tensor(workspace, "uint8", "workspace")
+    st = _lib().mixed_attention_fwd(ctypes.byref(layout), ctypes.byref(batch.struct),
+                                    q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                    float(sm_scale), out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), _stream_handle(stream))
+    if st:
+        raise MabError(st, "mixed_attention_fwd")
+
+
+def mab_status_string(status):
+    return _lib().mab_status_string(int(status)).decode()

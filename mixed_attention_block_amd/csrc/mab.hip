@@ -1,0 +1,810 @@
+// Mixed-batch attention over a paged, block-quantized KV cache, for gfx950.
+//
+// Operations follow the MBufo page "自研RDNA高併發推論引擎 以AI Max+ 395為範例":
+//   section 1  -- chunk rows and decode rows share one ForwardBatch and one
+//                 attention kernel (one launch serves both row kinds here);
+//   section 2  -- KV modes table: 32-value blocks with one fp16 scale, 34 bytes
+//                 (8-bit codes) or 18 bytes (4-bit codes), bit-exact codec.
+//
+// Kernels:
+//   append_kernel     -- encode new K/V rows into blocks at their page slots.
+//   attention_kernel  -- one launch over a flat list of work items: chunk
+//                        tiles first (heavy), then decode splits.  Each item
+//                        dequantizes its KV tiles into LDS as fp16, runs
+//                        S^T = K Q^T and O^T = V^T P^T on 16x16x32 fp16 MFMA
+//                        with fp32 accumulation and an fp32 online softmax.
+//   combine_kernel    -- log-sum-exp merge of split-K partials, ascending
+//                        split order, for rows whose keys span several splits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mab.h"
+
+namespace {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;       // attention work-group: 4 waves
+constexpr int kWaves = 4;
+constexpr int kStepKeys = 32;       // keys per LDS tile
+constexpr int kDecodeSplit = 512;   // keys per decode split (multiple of kStepKeys)
+constexpr int kChunkSplit = 32768;  // keys per chunk split (multiple of kStepKeys)
+constexpr int kChunkRows = 32;      // query rows per chunk tile
+constexpr int kMaxGroup = 8;        // query heads per KV head
+constexpr int kMaxGroupsPerWave = 4;  // 16-slot query groups per wave (chunk)
+constexpr int kMaxSeqs = 4096;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int F> struct Fmt;
+template <> struct Fmt<MAB_KV_Q8> { static constexpr int kBytes = 34; static constexpr int kQmax = 127; };
+template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static constexpr int kQmax = 7; };
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Work-item bookkeeping shared by host and device.  A sequence with more than
+// one row is a chunk: ceil(q_len/32) row tiles x Hkv x ceil(ctx/kChunkSplit)
+// key splits.  A one-row sequence is a decode row: Hkv x ceil(ctx/kDecodeSplit).
+struct SeqPlan {
+  int is_chunk, n_qt, n_split, items;
+};
+
+__host__ __device__ inline SeqPlan plan_seq(int q_len, int prefix, int hkv) {
+  SeqPlan p;
+  const int ctx = prefix + q_len;
+  p.is_chunk = q_len > 1;
+  p.n_qt = p.is_chunk ? ceil_div(q_len, kChunkRows) : 1;
+  p.n_split = ceil_div(ctx, p.is_chunk ? kChunkSplit : kDecodeSplit);
+  p.items = p.n_qt * hkv * p.n_split;
+  return p;
+}
+
+// Partial-result slots: chunk items own G*32 slots, decode items own G slots.
+__host__ __device__ inline int64_t partial_base(int64_t item, int64_t n_chunk_items, int group) {
+  const int64_t cs = (int64_t)group * kChunkRows;
+  return item < n_chunk_items ? item * cs : n_chunk_items * cs + (item - n_chunk_items) * group;
+}
+
+__host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct WsLayout {
+  int64_t o_off, ml_off, row_seq_off, seq_base_off, total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int64_t n_partials, int num_rows, int num_seqs, int head_dim) {
+  WsLayout w;
+  w.o_off = 0;
+  w.ml_off = align256(w.o_off + n_partials * head_dim * 4);
+  w.row_seq_off = align256(w.ml_off + n_partials * 8);
+  w.seq_base_off = align256(w.row_seq_off + (int64_t)num_rows * 4);
+  w.total = align256(w.seq_base_off + (int64_t)num_seqs * 4);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Append: one thread encodes one 32-value block.
+// ---------------------------------------------------------------------------
+
+__device__ inline int find_seq(const int32_t* __restrict__ q_start, int num_seqs, int row) {
+  int lo = 0, hi = num_seqs - 1;  // largest s with q_start[s] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (q_start[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int F>
+__device__ inline void encode_block(const half_t* __restrict__ x, uint8_t* __restrict__ dst) {
+  constexpr int Q = Fmt<F>::kQmax;
+  float xf[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half8_t v = *reinterpret_cast<const half8_t*>(x + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xf[8 * i + e] = (float)v[e];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xf[i]));
+  int code[32];
+  uint16_t dbits = 0;
+  if (amax > 0.f) {
+    const float s = amax / (float)Q;                 // IEEE binary32 divide
+    const half_t d = (half_t)s;                      // RNE, fp16 subnormals kept
+    dbits = __builtin_bit_cast(uint16_t, d);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float r = rintf(xf[i] / s);                    // half to even
+      r = fminf(fmaxf(r, -(float)Q), (float)Q);
+      code[i] = (int)r;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) code[i] = 0;
+  }
+  uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);  // blocks start on even bytes
+  d16[0] = dbits;
+  if constexpr (F == MAB_KV_Q8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      d16[1 + i] = (uint16_t)((code[2 * i] & 0xFF) | ((code[2 * i + 1] & 0xFF) << 8));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b0 = (code[4 * i] & 0xF) | ((code[4 * i + 1] & 0xF) << 4);
+      const int b1 = (code[4 * i + 2] & 0xF) | ((code[4 * i + 3] & 0xF) << 4);
+      d16[1 + i] = (uint16_t)(b0 | (b1 << 8));
+    }
+  }
+}
+
+template <int KF, int VF>
+__global__ void __launch_bounds__(256)
+append_kernel(const half_t* __restrict__ k_new, const half_t* __restrict__ v_new,
+              uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+              const int32_t* __restrict__ q_start, const int32_t* __restrict__ prefix_len,
+              const int32_t* __restrict__ block_table, int num_seqs, int num_rows,
+              int max_pages, int hkv, int head_dim, int page_size) {
+  const int nb = head_dim / 32;
+  const int64_t per_side = (int64_t)num_rows * hkv * nb;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= 2 * per_side) return;
+  const bool is_v = tid >= per_side;
+  const int64_t u = is_v ? tid - per_side : tid;
+  const int b = (int)(u % nb);
+  const int g = (int)((u / nb) % hkv);
+  const int row = (int)(u / ((int64_t)nb * hkv));
+  const int s = find_seq(q_start, num_seqs, row);
+  const int pos = prefix_len[s] + (row - q_start[s]);
+  const int page = block_table[(int64_t)s * max_pages + pos / page_size];
+  const int slot = pos % page_size;
+  const int64_t tok = ((int64_t)page * hkv + g) * page_size + slot;
+  const half_t* src = (is_v ? v_new : k_new) + ((int64_t)row * hkv + g) * head_dim + 32 * b;
+  if (is_v) encode_block<VF>(src, v_pool + (tok * nb + b) * Fmt<VF>::kBytes);
+  else encode_block<KF>(src, k_pool + (tok * nb + b) * Fmt<KF>::kBytes);
+}
+
+// ---------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------
+
+// Reads the byte-aligned 8 codes (or 4 bytes of nibbles) of a block through
+// 16-bit loads: blocks are 34 or 18 bytes long, so they only start on even
+// byte addresses.
+__device__ inline uint32_t load_u32_even(const uint8_t* p) {
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+  return (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+}
+
+template <int F>
+__device__ inline void dequant8(const uint8_t* blk, int j, half_t out[8]) {
+  // values 8j .. 8j+7 of the block at blk, as fp16(code * d)
+  const half_t d = __builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(blk));
+  if constexpr (F == MAB_KV_Q8) {
+    const uint32_t w0 = load_u32_even(blk + 2 + 8 * j);
+    const uint32_t w1 = load_u32_even(blk + 2 + 8 * j + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = (half_t)(float)(int8_t)(w0 >> (8 * e)) * d;
+      out[4 + e] = (half_t)(float)(int8_t)(w1 >> (8 * e)) * d;
+    }
+  } else {
+    const uint32_t w = load_u32_even(blk + 2 + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int nib = (int)((w >> (4 * e)) & 0xF);
+      out[e] = (half_t)(float)(nib >= 8 ? nib - 16 : nib) * d;
+    }
+  }
+}
+
+template <int NB>
+struct Tile {
+  static constexpr int kD = 32 * NB;
+  static constexpr int kKStride = kD + 8;         // halves per K row (16-byte rows, skewed)
+  static constexpr int kVStride = kStepKeys + 8;  // halves per V^T row
+  half_t k[kStepKeys * kKStride];                 // K_hat  [key][dim]
+  half_t vt[kD * kVStride];                       // V_hat^T [dim][key]
+};
+
+struct ItemCtx {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* bt_row;  // block-table row of the sequence
+  int hkv, g, page_size;
+};
+
+// Dequantize keys [kbase, kbase+32) of KV head g into tile t; keys >= kend are zero.
+// Executed by threads [0, nthr) of the caller's set (index `tid`).
+template <int NB, int KF, int VF>
+__device__ inline void produce_tile(Tile<NB>& t, const ItemCtx& c, int kbase, int kend, int tid, int nthr) {
+  constexpr int D = 32 * NB;
+  constexpr int KB = Fmt<KF>::kBytes, VB = Fmt<VF>::kBytes;
+  // K: unit = (key, block b, 8-value group j)
+  for (int u = tid; u < kStepKeys * NB * 4; u += nthr) {
+    const int kk = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
+    const int key = kbase + kk;
+    half_t v[8];
+    if (key < kend) {
+      const int page = c.bt_row[key / c.page_size];
+      const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + key % c.page_size;
+      dequant8<KF>(c.k_pool + (tok * NB + b) * KB, j, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (half_t)0.f;
+    }
+    half8_t h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = v[e];
+    *reinterpret_cast<half8_t*>(&t.k[kk * Tile<NB>::kKStride + 32 * b + 8 * j]) = h;
+  }
+  // V^T: unit = (key pair, block b, 8-value group j)
+  for (int u = tid; u < (kStepKeys / 2) * NB * 4; u += nthr) {
+    const int kp = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
+    half_t v0[8], v1[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = kbase + 2 * kp + h;
+      half_t* v = h ? v1 : v0;
+      if (key < kend) {
+        const int page = c.bt_row[key / c.page_size];
+        const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + key % c.page_size;
+        dequant8<VF>(c.v_pool + (tok * NB + b) * VB, j, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (half_t)0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      half2_t pr;
+      pr[0] = v0[e];
+      pr[1] = v1[e];
+      *reinterpret_cast<half2_t*>(&t.vt[(32 * b + 8 * j + e) * Tile<NB>::kVStride + 2 * kp]) = pr;
+    }
+  }
+  (void)D;
+}
+
+// Online-softmax state of one 16-slot query group held by one wave.
+// Lane l serves slot l%16; the four lanes of a slot hold different keys of S^T
+// and different dims of O^T.
+template <int NB>
+struct Group {
+  half8_t q[NB];          // Q^T operand: slot l%16, dims 32b + 8(l/16) + [0,8)
+  float4_t o[2 * NB];     // O^T: slot l%16, dims 16t + 4(l/16) + [0,4)
+  float m, l;             // running max (log2 units) and lane-partial sum
+  int limit;              // last key position visible to the slot (-1: none)
+};
+
+template <int NB>
+__device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (qrow) gr.q[b] = *reinterpret_cast<const half8_t*>(qrow + 32 * b + 8 * (lane >> 4));
+    else gr.q[b] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int t = 0; t < 2 * NB; ++t) gr.o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  gr.m = -INFINITY;
+  gr.l = 0.f;
+  gr.limit = qrow ? limit : -1;
+}
+
+// One 32-key step of one group against tile t.
+template <int NB>
+__device__ inline void group_step(Group<NB>& gr, const Tile<NB>& t, const half8_t (&kf)[2][NB],
+                                  int kbase, int kend, float c, int lane) {
+  float4_t s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kt][b], gr.q[b], s[kt], 0, 0, 0);
+  }
+  // scores in log2 units, masked by position
+  float z[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kbase + 16 * kt + 4 * (lane >> 4) + i;
+      const bool ok = key <= gr.limit && key < kend;
+      z[kt][i] = ok ? s[kt][i] * c : -INFINITY;
+      mx = fmaxf(mx, z[kt][i]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(gr.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(gr.m - m_use);
+  float psum = 0.f;
+  half8_t pf;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(z[kt][i] - m_use);
+      psum += p;
+      pf[4 * kt + i] = (half_t)p;
+    }
+  gr.l = gr.l * alpha + psum;
+  gr.m = m_new;
+#pragma unroll
+  for (int tt = 0; tt < 2 * NB; ++tt) {
+    gr.o[tt] *= alpha;
+    // V^T operand: dim 16tt + l%16, keys 4(l/16)+[0,4) and 16+4(l/16)+[0,4)
+    const half_t* vr = &t.vt[(16 * tt + (lane & 15)) * Tile<NB>::kVStride + 4 * (lane >> 4)];
+    const half4_t a0 = *reinterpret_cast<const half4_t*>(vr);
+    const half4_t a1 = *reinterpret_cast<const half4_t*>(vr + 16);
+    const half8_t vf = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    gr.o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, gr.o[tt], 0, 0, 0);
+  }
+}
+
+template <int NB>
+__device__ inline void load_kfrag(half8_t (&kf)[2][NB], const Tile<NB>& t, int lane) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      kf[kt][b] = *reinterpret_cast<const half8_t*>(
+          &t.k[(16 * kt + (lane & 15)) * Tile<NB>::kKStride + 32 * b + 8 * (lane >> 4)]);
+}
+
+struct AttnArgs {
+  const half_t* q;
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* q_start;
+  const int32_t* prefix_len;
+  const int32_t* block_table;
+  float* out;
+  float* o_part;
+  float2* ml_part;
+  int32_t* row_seq;
+  int32_t* seq_base;
+  int64_t n_partials;
+  int num_seqs, num_rows, max_pages;
+  int hq, hkv, page_size;
+  int n_chunk_items, n_items;
+  float c;  // sm_scale * log2(e)
+};
+
+// Locates work item `item` by scanning the per-sequence item counts (chunk
+// sequences first, then decode sequences, each in sequence order).
+struct Found {
+  int s, local, item_base;
+};
+
+__device__ inline bool locate_item(const AttnArgs& a, int item, Found& f, int* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = ceil_div(a.num_seqs, kThreads);
+  const int s0 = min(a.num_seqs, tid * per), s1 = min(a.num_seqs, s0 + per);
+  int c = 0, d = 0;
+  for (int s = s0; s < s1; ++s) {
+    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv);
+    if (p.is_chunk) c += p.items; else d += p.items;
+  }
+  int ci = c, di = d;  // inclusive wave scan
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int tc = __shfl_up(ci, off), td = __shfl_up(di, off);
+    if (lane >= off) { ci += tc; di += td; }
+  }
+  if (lane == 63) { sh[wave] = ci; sh[4 + wave] = di; }
+  if (tid == 0) sh[8] = -1;
+  __syncthreads();
+  int cb = ci - c, db = di - d, ctot = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) { cb += sh[w]; db += sh[4 + w]; }
+    ctot += sh[w];
+  }
+  for (int s = s0; s < s1; ++s) {
+    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv);
+    const int base = p.is_chunk ? cb : ctot + db;
+    if (item >= base && item < base + p.items) { sh[8] = s; sh[9] = item - base; sh[10] = base; }
+    if (p.is_chunk) cb += p.items; else db += p.items;
+  }
+  __syncthreads();
+  f.s = sh[8];
+  f.local = sh[9];
+  f.item_base = sh[10];
+  __syncthreads();
+  return f.s >= 0 && ctot == a.n_chunk_items;
+}
+
+template <int NB, int KF, int VF>
+__global__ void __launch_bounds__(kThreads)
+attention_kernel(AttnArgs a) {
+  constexpr int D = 32 * NB;
+  __shared__ Tile<NB> tiles[kWaves];
+  __shared__ int sh[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int item = blockIdx.x;
+
+  Found f;
+  if (!locate_item(a, item, f, sh)) return;
+  const int s = f.s;
+  const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
+  const int ctx = prefix + q_len;
+  const SeqPlan p = plan_seq(q_len, prefix, a.hkv);
+  const int G = a.hq / a.hkv;
+
+  int qt, g, j;
+  if (p.is_chunk) {
+    qt = f.local % p.n_qt;
+    const int rest = f.local / p.n_qt;
+    j = rest % p.n_split;
+    g = rest / p.n_split;
+  } else {
+    qt = 0;
+    j = f.local % p.n_split;
+    g = f.local / p.n_split;
+  }
+  if (tid == 0 && f.local == 0) a.seq_base[s] = f.item_base;
+  if (g == 0 && j == 0) {
+    const int rows = p.is_chunk ? kChunkRows : 1;
+    for (int r = tid; r < rows; r += kThreads) {
+      const int i = qt * kChunkRows + r;
+      if (i < q_len) a.row_seq[r0 + i] = s;
+    }
+  }
+
+  const int split = p.is_chunk ? kChunkSplit : kDecodeSplit;
+  const int kb = j * split;
+  int ke = min(ctx, kb + split);
+  if (p.is_chunk) {
+    const int last_row = min(q_len, (qt + 1) * kChunkRows) - 1;
+    ke = min(ke, prefix + last_row + 1);
+    if (kb >= ke) return;  // no row of this tile sees this split
+  }
+  const int nsteps = ceil_div(ke - kb, kStepKeys);
+  const int64_t pbase = partial_base(item, a.n_chunk_items, G);
+  const bool single = p.n_split == 1;
+
+  ItemCtx ic;
+  ic.k_pool = a.k_pool;
+  ic.v_pool = a.v_pool;
+  ic.bt_row = a.block_table + (int64_t)s * a.max_pages;
+  ic.hkv = a.hkv;
+  ic.g = g;
+  ic.page_size = a.page_size;
+
+  if (!p.is_chunk) {
+    // Decode split: the four waves take interleaved 32-key steps, each with a
+    // private tile, then merge their softmax states in fixed wave order.
+    Group<NB> gr;
+    const int n = lane & 15;
+    const half_t* qrow = n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr;
+    group_init(gr, qrow, ctx - 1, lane);
+    for (int sb = 0; sb < nsteps; sb += kWaves) {
+      const int st = sb + wave;
+      const int kbase = kb + st * kStepKeys;
+      if (st < nsteps) produce_tile<NB, KF, VF>(tiles[wave], ic, kbase, ke, lane, 64);
+      __syncthreads();
+      if (st < nsteps) {
+        half8_t kf[2][NB];
+        load_kfrag(kf, tiles[wave], lane);
+        group_step(gr, tiles[wave], kf, kbase, ke, a.c, lane);
+      }
+      __syncthreads();
+    }
+    float lsum = gr.l;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    // merge buffers alias the tiles (all reads of tiles are done)
+    float* mo = reinterpret_cast<float*>(&tiles[0]);     // [wave][16][D]
+    float* mm = mo + kWaves * 16 * D;                    // [wave][16]
+    float* ml = mm + kWaves * 16;                        // [wave][16]
+#pragma unroll
+    for (int tt = 0; tt < 2 * NB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo[(wave * 16 + n) * D + 16 * tt + 4 * (lane >> 4) + i] = gr.o[tt][i];
+    if (lane < 16) { mm[wave * 16 + n] = gr.m; ml[wave * 16 + n] = lsum; }
+    __syncthreads();
+    for (int u = tid; u < G * D; u += kThreads) {
+      const int hl = u / D, dd = u % D;
+      float M = -INFINITY;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + hl]);
+      float L = 0.f, O = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(mm[w * 16 + hl] - M);
+        L += ml[w * 16 + hl] * sc;
+        O += mo[(w * 16 + hl) * D + dd] * sc;
+      }
+      const int h = g * G + hl;
+      if (single) {
+        a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / L;
+      } else {
+        const int64_t pi = pbase + hl;
+        if (pi < a.n_partials) {
+          a.o_part[pi * D + dd] = O;
+          if (dd == 0) a.ml_part[pi] = make_float2(M, L);
+        }
+      }
+    }
+    return;
+  }
+
+  // Chunk tile: 32 rows x G heads = 2G groups of 16 slots, dealt round-robin to
+  // the four waves; all waves share one tile per step.
+  Group<NB> grs[kMaxGroupsPerWave];
+  const int ngroups = 2 * G;
+#pragma unroll
+  for (int k = 0; k < kMaxGroupsPerWave; ++k) {
+    const int gi = wave + kWaves * k;
+    const int hl = gi >> 1, half_rows = gi & 1;
+    const int i = qt * kChunkRows + 16 * half_rows + (lane & 15);
+    const half_t* qrow = (gi < ngroups && i < q_len) ? a.q + ((int64_t)(r0 + i) * a.hq + g * G + hl) * D
+                                                     : nullptr;
+    group_init(grs[k], qrow, prefix + i, lane);
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    const int kbase = kb + st * kStepKeys;
+    produce_tile<NB, KF, VF>(tiles[0], ic, kbase, ke, tid, kThreads);
+    __syncthreads();
+    half8_t kf[2][NB];
+    load_kfrag(kf, tiles[0], lane);
+#pragma unroll
+    for (int k = 0; k < kMaxGroupsPerWave; ++k)
+      if (wave + kWaves * k < ngroups) group_step(grs[k], tiles[0], kf, kbase, ke, a.c, lane);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxGroupsPerWave; ++k) {
+    const int gi = wave + kWaves * k;
+    if (gi >= ngroups) continue;
+    const int hl = gi >> 1, half_rows = gi & 1;
+    const int r = 16 * half_rows + (lane & 15);
+    const int i = qt * kChunkRows + r;
+    float lsum = grs[k].l;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (i >= q_len) continue;
+    const int h = g * G + hl;
+    if (single) {
+      const float inv = 1.f / lsum;
+      float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * (lane >> 4);
+#pragma unroll
+      for (int tt = 0; tt < 2 * NB; ++tt) *reinterpret_cast<float4_t*>(dst + 16 * tt) = grs[k].o[tt] * inv;
+    } else {
+      const int64_t pi = pbase + (int64_t)hl * kChunkRows + r;
+      if (pi < a.n_partials) {
+        float* dst = a.o_part + pi * D + 4 * (lane >> 4);
+#pragma unroll
+        for (int tt = 0; tt < 2 * NB; ++tt) *reinterpret_cast<float4_t*>(dst + 16 * tt) = grs[k].o[tt];
+        if (lane < 16) a.ml_part[pi] = make_float2(grs[k].m, lsum);
+      }
+    }
+  }
+}
+
+// Merges the split-K partials of rows whose keys span several splits, in
+// ascending split order.  One work-group per row.
+__global__ void __launch_bounds__(256)
+combine_kernel(AttnArgs a, int head_dim) {
+  const int row = blockIdx.x;
+  const int s = a.row_seq[row];
+  if (s < 0 || s >= a.num_seqs) return;
+  const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
+  const SeqPlan p = plan_seq(q_len, prefix, a.hkv);
+  if (p.n_split == 1) return;
+  const int item_base = a.seq_base[s];
+  const int G = a.hq / a.hkv;
+  const int i = row - r0;
+  if (i < 0 || i >= q_len || item_base < 0 || item_base >= a.n_items) return;
+  const int pos = prefix + i;
+  const int split = p.is_chunk ? kChunkSplit : kDecodeSplit;
+  const int nj = pos / split + 1;
+  const int qt = i / kChunkRows, rr = i % kChunkRows;
+  for (int u = threadIdx.x; u < a.hq * head_dim; u += blockDim.x) {
+    const int h = u / head_dim, dd = u % head_dim;
+    const int g = h / G, hl = h % G;
+    float M = -INFINITY;
+    for (int j = 0; j < nj; ++j) {
+      const int item = p.is_chunk ? item_base + qt + p.n_qt * (j + p.n_split * g)
+                                  : item_base + g * p.n_split + j;
+      const int64_t pi = partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
+      if (pi >= a.n_partials) return;
+      M = fmaxf(M, a.ml_part[pi].x);
+    }
+    float L = 0.f, O = 0.f;
+    for (int j = 0; j < nj; ++j) {
+      const int item = p.is_chunk ? item_base + qt + p.n_qt * (j + p.n_split * g)
+                                  : item_base + g * p.n_split + j;
+      const int64_t pi = partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
+      const float2 ml = a.ml_part[pi];
+      const float sc = __builtin_amdgcn_exp2f(ml.x - M);
+      L += ml.y * sc;
+      O += a.o_part[pi * head_dim + dd] * sc;
+    }
+    a.out[((int64_t)row * a.hq + h) * head_dim + dd] = O / L;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+bool fmt_ok(int32_t f) { return f == MAB_KV_Q8 || f == MAB_KV_Q4; }
+
+int check_layout(const mab_kv_layout* L) {
+  if (!L) return MAB_ERR_NULL;
+  if (L->num_q_heads < 1 || L->num_kv_heads < 1 || L->num_q_heads % L->num_kv_heads) return MAB_ERR_SHAPE;
+  if (L->head_dim < 32 || L->head_dim % 32 || L->page_size < 16 || L->page_size % 16) return MAB_ERR_SHAPE;
+  if (L->num_pages < 1 || !fmt_ok(L->k_format) || !fmt_ok(L->v_format) || L->reserved) return MAB_ERR_SHAPE;
+  if (L->head_dim != 64 && L->head_dim != 128) return MAB_ERR_UNSUPPORTED;
+  if (L->num_q_heads / L->num_kv_heads > kMaxGroup) return MAB_ERR_UNSUPPORTED;
+  return MAB_OK;
+}
+
+struct HostPlan {
+  int64_t n_chunk_items = 0, n_items = 0, n_partials = 0;
+};
+
+int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
+  if (!B) return MAB_ERR_NULL;
+  if (B->num_seqs < 0 || B->num_rows < 0 || B->max_pages_per_seq < 1 || B->reserved) return MAB_ERR_SHAPE;
+  if (B->num_seqs > kMaxSeqs) return MAB_ERR_UNSUPPORTED;
+  if (B->num_seqs == 0) return B->num_rows == 0 ? MAB_OK : MAB_ERR_SHAPE;
+  if (!B->q_start || !B->prefix_len || !B->block_table || !B->q_start_host || !B->prefix_len_host)
+    return MAB_ERR_NULL;
+  if (B->q_start_host[0] != 0 || B->q_start_host[B->num_seqs] != B->num_rows) return MAB_ERR_SHAPE;
+  const int G = L->num_q_heads / L->num_kv_heads;
+  int64_t chunk = 0, dec = 0;
+  for (int s = 0; s < B->num_seqs; ++s) {
+    const int64_t q_len = (int64_t)B->q_start_host[s + 1] - B->q_start_host[s];
+    const int64_t prefix = B->prefix_len_host[s];
+    if (q_len < 1 || prefix < 0) return MAB_ERR_SHAPE;
+    const int64_t ctx = prefix + q_len;
+    if (ctx > (int64_t)B->max_pages_per_seq * L->page_size || ctx > (int64_t)1 << 30) return MAB_ERR_SHAPE;
+    const SeqPlan p = plan_seq((int)q_len, (int)prefix, L->num_kv_heads);
+    if (p.is_chunk) chunk += p.items; else dec += p.items;
+  }
+  if (chunk + dec > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
+  if (hp) {
+    hp->n_chunk_items = chunk;
+    hp->n_items = chunk + dec;
+    hp->n_partials = chunk * G * kChunkRows + dec * G;
+  }
+  return MAB_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+template <int KF, int VF>
+void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, const void* vn, void* kp,
+                   void* vp, hipStream_t st) {
+  const int64_t n = 2LL * B->num_rows * L->num_kv_heads * (L->head_dim / 32);
+  const int grid = (int)((n + 255) / 256);
+  hipLaunchKernelGGL((append_kernel<KF, VF>), dim3(grid), dim3(256), 0, st, (const half_t*)kn,
+                     (const half_t*)vn, (uint8_t*)kp, (uint8_t*)vp, B->q_start, B->prefix_len,
+                     B->block_table, B->num_seqs, B->num_rows, B->max_pages_per_seq, L->num_kv_heads,
+                     L->head_dim, L->page_size);
+}
+
+template <int NB, int KF, int VF>
+void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
+}
+
+template <int NB>
+void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st) {
+  if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st);
+  else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st);
+  else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st);
+  else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_block_bytes(int32_t format) {
+  return format == MAB_KV_Q8 ? 34 : format == MAB_KV_Q4 ? 18 : 0;
+}
+
+int64_t kv_pool_bytes(const mab_kv_layout* layout, int32_t format) {
+  if (!layout || !fmt_ok(format) || layout->num_pages < 1 || layout->num_kv_heads < 1 ||
+      layout->page_size < 1 || layout->head_dim < 32 || layout->head_dim % 32)
+    return -1;
+  return (int64_t)layout->num_pages * layout->num_kv_heads * layout->page_size * (layout->head_dim / 32) *
+         kv_block_bytes(format);
+}
+
+int64_t attention_workspace_bytes(const mab_kv_layout* layout, const mab_batch* batch) {
+  int st = check_layout(layout);
+  if (st) return -st;
+  HostPlan hp;
+  st = check_batch(layout, batch, &hp);
+  if (st) return -st;
+  return ws_layout(hp.n_partials, batch->num_rows, batch->num_seqs, layout->head_dim).total;
+}
+
+int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch, const void* k_new,
+                        const void* v_new, void* k_pool, void* v_pool, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  st = check_batch(layout, batch, nullptr);
+  if (st) return st;
+  if (batch->num_rows == 0) return MAB_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool) return MAB_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)) return MAB_ERR_ALIGN;
+  hipStream_t hs = (hipStream_t)stream;
+  const int kf = layout->k_format, vf = layout->v_format;
+  if (kf == MAB_KV_Q8 && vf == MAB_KV_Q8) launch_append<MAB_KV_Q8, MAB_KV_Q8>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  else if (kf == MAB_KV_Q8) launch_append<MAB_KV_Q8, MAB_KV_Q4>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  else if (vf == MAB_KV_Q8) launch_append<MAB_KV_Q4, MAB_KV_Q8>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  else launch_append<MAB_KV_Q4, MAB_KV_Q4>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
+}
+
+int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
+                            const void* k_pool, const void* v_pool, float sm_scale, float* out,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  HostPlan hp;
+  st = check_batch(layout, batch, &hp);
+  if (st) return st;
+  if (batch->num_rows == 0) return MAB_OK;
+  if (!q || !k_pool || !v_pool || !out || !workspace) return MAB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
+    return MAB_ERR_ALIGN;
+  const WsLayout wl = ws_layout(hp.n_partials, batch->num_rows, batch->num_seqs, layout->head_dim);
+  if (workspace_bytes < wl.total) return MAB_ERR_WORKSPACE;
+
+  char* ws = (char*)workspace;
+  AttnArgs a;
+  a.q = (const half_t*)q;
+  a.k_pool = (const uint8_t*)k_pool;
+  a.v_pool = (const uint8_t*)v_pool;
+  a.q_start = batch->q_start;
+  a.prefix_len = batch->prefix_len;
+  a.block_table = batch->block_table;
+  a.out = out;
+  a.o_part = (float*)(ws + wl.o_off);
+  a.ml_part = (float2*)(ws + wl.ml_off);
+  a.row_seq = (int32_t*)(ws + wl.row_seq_off);
+  a.seq_base = (int32_t*)(ws + wl.seq_base_off);
+  a.n_partials = hp.n_partials;
+  a.num_seqs = batch->num_seqs;
+  a.num_rows = batch->num_rows;
+  a.max_pages = batch->max_pages_per_seq;
+  a.hq = layout->num_q_heads;
+  a.hkv = layout->num_kv_heads;
+  a.page_size = layout->page_size;
+  a.n_chunk_items = (int)hp.n_chunk_items;
+  a.n_items = (int)hp.n_items;
+  a.c = sm_scale * kLog2e;
+
+  hipStream_t hs = (hipStream_t)stream;
+  const int grid = (int)hp.n_items;
+  if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
+  else launch_attention_nb<4>(layout, a, grid, hs);
+  if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
+  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows), dim3(256), 0, hs, a, layout->head_dim);
+  return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
+}
+
+const char* mab_status_string(int32_t status) {
+  switch (status) {
+    case MAB_OK: return "ok";
+    case MAB_ERR_NULL: return "a required pointer is NULL";
+    case MAB_ERR_SHAPE: return "a layout or batch field breaks a stated rule";
+    case MAB_ERR_UNSUPPORTED: return "shape outside the supported set";
+    case MAB_ERR_WORKSPACE: return "workspace smaller than attention_workspace_bytes()";
+    case MAB_ERR_ALIGN: return "a device buffer is not 16-byte aligned";
+    case MAB_ERR_HIP: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

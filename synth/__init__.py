@@ -28,7 +28,8 @@ Workloads (one attention layer each unless stated):
 * ``step_k4v4``       -- one layer of the full-step stress: K4V4, 16 decode rows
                          with contexts log-uniform in [512, 262144] and a
                          2048-row chunk at 131072; K outliers.  The step has 12
-                         such layers, seeded ``seed * 100 + layer``.
+                         such layers sharing one batch; layer l draws its values
+                         with ``value_seed = seed * 100 + l``.
 * ``small_mixed``     -- a mid-size parity case: 24/4 heads, head_dim 128,
                          page 32, several chunks and decode rows with ragged
                          lengths (not a benchmark workload).
@@ -118,10 +119,12 @@ WORKLOADS = ("tiny_mixed", "small_mixed", "decode16", "mixed16_chunk2k",
 
 
 def make_case(name, seed, device="cpu", seqs=None, spare_pages=3, with_values=True,
-              **overrides):
+              value_seed=None, **overrides):
     """Build a seeded case.  ``seqs`` (list of (prefix_len, q_len)) and the
     keyword overrides (hq, hkv, d, kf, vf, ps, outliers) allow custom shapes
-    for edge-case tests."""
+    for edge-case tests.  The batch structure comes from ``seed``; values come
+    from ``value_seed`` (default ``seed``), so the layers of one step share a
+    batch and differ in their values."""
     rng = np.random.Generator(np.random.PCG64(seed))
     try:
         spec = _spec(name)
@@ -157,7 +160,7 @@ def make_case(name, seed, device="cpu", seqs=None, spare_pages=3, with_values=Tr
     layout = dict(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
                   num_pages=num_pages, k_format=spec["kf"], v_format=spec["vf"])
     sm_scale = float(np.float32(1.0 / np.sqrt(d)))
-    case = Case(name=name, seed=seed, layout=layout, q_start=q_start, prefix_len=prefix_len,
+    case = Case(name=name, seed=seed if value_seed is None else value_seed, layout=layout, q_start=q_start, prefix_len=prefix_len,
                 block_table=block_table, q=None, k_new=None, v_new=None,
                 sm_scale=sm_scale, outlier_channels=outlier_channels)
     if with_values:

@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/mab.h declares, sizes pools and workspaces by the closed forms,
+and rejects malformed calls with a status before touching the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mixed_attention_block_amd as mab
+from oracle import cache as oracle_cache
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mab.h")
+FAKE_DEV = 0x7F0000000000  # never dereferenced on the host paths exercised here
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"kv_append_quant", "mixed_attention_fwd", "attention_workspace_bytes",
+            "kv_pool_bytes", "kv_block_bytes", "mab_status_string"} <= set(names)
+    lib = ctypes.CDLL(mab.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_block_and_pool_sizes():
+    assert mab.kv_block_bytes("q8") == 34 and mab.kv_block_bytes("q4") == 18
+    assert mab.kv_block_bytes(99) == 0
+    for kf, vf in (("q8", "q8"), ("q4", "q4"), ("q8", "q4")):
+        lay = mab.make_layout(24, 4, 128, 256, 77, kf, vf)
+        d = dict(num_q_heads=24, num_kv_heads=4, head_dim=128, page_size=256, num_pages=77)
+        assert mab.kv_pool_bytes(lay, kf) == oracle_cache.pool_bytes(d, kf)
+        assert mab.kv_pool_bytes(lay, vf) == oracle_cache.pool_bytes(d, vf)
+    assert mab.kv_pool_bytes(mab.make_layout(24, 4, 100, 256, 77), "q8") == -1
+
+
+def test_status_strings():
+    for st in range(7):
+        assert mab.mab_status_string(st)
+    assert "unknown" in mab.mab_status_string(1234)
+
+
+class _HostBatch:
+    def __init__(self, q_start, prefix_len, max_pages=64, dev_ptrs=True):
+        self.qs = np.ascontiguousarray(q_start, np.int32)
+        self.pl = np.ascontiguousarray(prefix_len, np.int32)
+        ptr = FAKE_DEV if dev_ptrs else 0
+        self.struct = mab.Batch(len(self.pl), int(self.qs[-1]), max_pages, 0, ptr, ptr, ptr,
+                                self.qs.ctypes.data, self.pl.ctypes.data)
+
+
+def _ws(layout, batch):
+    return mab._lib().attention_workspace_bytes(ctypes.byref(layout), ctypes.byref(batch.struct))
+
+
+def test_workspace_closed_form():
+    lay = mab.make_layout(24, 4, 128, 256, 1000)
+    b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
+    n = _ws(lay, b)
+    # decode items: 4 heads x ceil(ctx/512); chunk: 2 tiles x 4 heads x 1 split, 32 rows x 6 heads each
+    dec_items = 4 * (-(-1001 // 512)) + 4 * (-(-70001 // 512))
+    chunk_items = 2 * 4 * 1
+    partials = chunk_items * 6 * 32 + dec_items * 6
+    assert n >= partials * (128 + 2) * 4
+    assert n < partials * (128 + 2) * 4 + 4 * 256 + 8 * 4
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(num_q_heads=25), 2), (dict(head_dim=96), 3), (dict(head_dim=48), 2),
+    (dict(page_size=24), 2), (dict(page_size=0), 2), (dict(k_format=3), 2),
+    (dict(num_q_heads=36, num_kv_heads=2), 3), (dict(num_pages=0), 2), (dict(reserved=1), 2),
+])
+def test_layout_errors(mutate, status):
+    base = dict(num_q_heads=24, num_kv_heads=4, head_dim=128, page_size=256, num_pages=100,
+                k_format=1, v_format=1, reserved=0)
+    base.update(mutate)
+    lay = mab.KVLayout(**base)
+    assert _ws(lay, _HostBatch([0, 1], [5])) == -status
+
+
+@pytest.mark.parametrize("q_start,prefix,max_pages,status", [
+    ([0, 1, 1], [5, 6], 64, 2),          # a sequence with no rows
+    ([1, 2], [5], 64, 2),                # q_start[0] != 0
+    ([0, 1], [-1], 64, 2),               # negative prefix
+    ([0, 1], [256 * 64], 64, 2),         # context beyond the block-table row
+    ([0, 3, 2], [0, 0], 64, 2),          # decreasing q_start
+])
+def test_batch_errors(q_start, prefix, max_pages, status):
+    lay = mab.make_layout(24, 4, 128, 256, 100)
+    assert _ws(lay, _HostBatch(q_start, prefix, max_pages)) == -status
+
+
+def test_null_and_alignment_and_workspace_errors():
+    lib = mab._lib()
+    lay = mab.make_layout(24, 4, 128, 256, 100)
+    b = _HostBatch([0, 1, 2], [10, 20])
+    L, B = ctypes.byref(lay), ctypes.byref(b.struct)
+    d = FAKE_DEV
+    assert lib.kv_append_quant(L, B, 0, d, d, d, None) == 1
+    assert lib.kv_append_quant(L, B, d + 2, d, d, d, None) == 5
+    assert lib.mixed_attention_fwd(L, B, d, d, d, 0.1, 0, d, 1 << 30, None) == 1
+    assert lib.mixed_attention_fwd(L, B, d, d + 8, d, 0.1, d, d, 1 << 30, None) == 5
+    assert lib.mixed_attention_fwd(L, B, d, d, d, 0.1, d, d, 16, None) == 4
+    nb = _HostBatch([0, 1, 2], [10, 20], dev_ptrs=False)
+    assert lib.mixed_attention_fwd(L, ctypes.byref(nb.struct), d, d, d, 0.1, d, d, 1 << 30, None) == 1
+    assert lib.kv_append_quant(None, B, d, d, d, d, None) == 1
+
+
+def test_empty_batch_is_a_no_op():
+    lib = mab._lib()
+    lay = mab.make_layout(24, 4, 128, 256, 100)
+    b = mab.Batch(0, 0, 1, 0, 0, 0, 0, 0, 0)
+    assert lib.kv_append_quant(ctypes.byref(lay), ctypes.byref(b), 0, 0, 0, 0, None) == 0
+    assert lib.mixed_attention_fwd(ctypes.byref(lay), ctypes.byref(b), 0, 0, 0, 0.1, 0, 0, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(mab, "LIB_PATH", "/nonexistent/libmab.so")
+    monkeypatch.setattr(mab, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        mab.kv_block_bytes("q8")
