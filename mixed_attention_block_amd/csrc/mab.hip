@@ -180,6 +180,27 @@ __device__ inline uint32_t load_u32_even(const uint8_t* p) {
   return (uint32_t)q[0] | ((uint32_t)q[1] << 16);
 }
 
+// Codes 8j .. 8j+7 of the block at blk as exact fp16 integers (no scale).
+template <int F>
+__device__ inline void codes8(const uint8_t* blk, int j, half_t out[8]) {
+  if constexpr (F == MAB_KV_Q8) {
+    const uint32_t w0 = load_u32_even(blk + 2 + 8 * j);
+    const uint32_t w1 = load_u32_even(blk + 2 + 8 * j + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = (half_t)(float)(int8_t)(w0 >> (8 * e));
+      out[4 + e] = (half_t)(float)(int8_t)(w1 >> (8 * e));
+    }
+  } else {
+    const uint32_t w = load_u32_even(blk + 2 + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int nib = (int)((w >> (4 * e)) & 0xF);
+      out[e] = (half_t)(float)(nib >= 8 ? nib - 16 : nib);
+    }
+  }
+}
+
 template <int F>
 __device__ inline void dequant8(const uint8_t* blk, int j, half_t out[8]) {
   // values 8j .. 8j+7 of the block at blk, as fp16(code * d)
@@ -207,8 +228,9 @@ struct Tile {
   static constexpr int kD = 32 * NB;
   static constexpr int kKStride = kD + 8;         // halves per K row (16-byte rows, skewed)
   static constexpr int kVStride = kStepKeys + 8;  // halves per V^T row
-  half_t k[kStepKeys * kKStride];                 // K_hat  [key][dim]
+  half_t k[kStepKeys * kKStride];                 // K codes [key][dim], exact fp16 integers
   half_t vt[kD * kVStride];                       // V_hat^T [dim][key]
+  float kd[NB * kStepKeys];                       // K scale * sm_scale * log2(e), [block][key]
 };
 
 struct ItemCtx {
@@ -221,7 +243,8 @@ struct ItemCtx {
 // Dequantize keys [kbase, kbase+32) of KV head g into tile t; keys >= kend are zero.
 // Executed by threads [0, nthr) of the caller's set (index `tid`).
 template <int NB, int KF, int VF>
-__device__ inline void produce_tile(Tile<NB>& t, const ItemCtx& c, int kbase, int kend, int tid, int nthr) {
+__device__ inline void produce_tile(Tile<NB>& t, const ItemCtx& c, int kbase, int kend, int tid, int nthr,
+                                    float zc) {
   constexpr int D = 32 * NB;
   constexpr int KB = Fmt<KF>::kBytes, VB = Fmt<VF>::kBytes;
   // K: unit = (key, block b, 8-value group j)
@@ -229,14 +252,18 @@ __device__ inline void produce_tile(Tile<NB>& t, const ItemCtx& c, int kbase, in
     const int kk = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
     const int key = kbase + kk;
     half_t v[8];
+    float kd = 0.f;
     if (key < kend) {
       const int page = c.bt_row[key / c.page_size];
       const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + key % c.page_size;
-      dequant8<KF>(c.k_pool + (tok * NB + b) * KB, j, v);
+      const uint8_t* blk = c.k_pool + (tok * NB + b) * KB;
+      codes8<KF>(blk, j, v);
+      kd = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(blk)) * zc;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (half_t)0.f;
     }
+    if (j == 0) t.kd[b * kStepKeys + kk] = kd;
     half8_t h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = v[e];
@@ -296,16 +323,22 @@ __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, 
 }
 
 // One 32-key step of one group against tile t.
+// Scores: one MFMA per 32-dim block on the exact integer codes, then the
+// block's scale (already multiplied by sm_scale*log2(e)) applied in fp32, so
+// the only roundings are fp32 ones.
 template <int NB>
 __device__ inline void group_step(Group<NB>& gr, const Tile<NB>& t, const half8_t (&kf)[2][NB],
-                                  int kbase, int kend, float c, int lane) {
+                                  const float4_t (&kd)[2][NB], int kbase, int kend, int lane) {
   float4_t s[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     s[kt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kt][b], gr.q[b], s[kt], 0, 0, 0);
+    for (int b = 0; b < NB; ++b) {
+      const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kt][b], gr.q[b],
+                                                                 float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      s[kt] += kd[kt][b] * pb;
+    }
   }
   // scores in log2 units, masked by position
   float z[2][4];
@@ -316,7 +349,7 @@ __device__ inline void group_step(Group<NB>& gr, const Tile<NB>& t, const half8_
     for (int i = 0; i < 4; ++i) {
       const int key = kbase + 16 * kt + 4 * (lane >> 4) + i;
       const bool ok = key <= gr.limit && key < kend;
-      z[kt][i] = ok ? s[kt][i] * c : -INFINITY;
+      z[kt][i] = ok ? s[kt][i] : -INFINITY;
       mx = fmaxf(mx, z[kt][i]);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -349,13 +382,15 @@ __device__ inline void group_step(Group<NB>& gr, const Tile<NB>& t, const half8_
 }
 
 template <int NB>
-__device__ inline void load_kfrag(half8_t (&kf)[2][NB], const Tile<NB>& t, int lane) {
+__device__ inline void load_kfrag(half8_t (&kf)[2][NB], float4_t (&kd)[2][NB], const Tile<NB>& t, int lane) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
       kf[kt][b] = *reinterpret_cast<const half8_t*>(
           &t.k[(16 * kt + (lane & 15)) * Tile<NB>::kKStride + 32 * b + 8 * (lane >> 4)]);
+      kd[kt][b] = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * (lane >> 4)]);
+    }
 }
 
 struct AttnArgs {
@@ -487,12 +522,13 @@ attention_kernel(AttnArgs a) {
     for (int sb = 0; sb < nsteps; sb += kWaves) {
       const int st = sb + wave;
       const int kbase = kb + st * kStepKeys;
-      if (st < nsteps) produce_tile<NB, KF, VF>(tiles[wave], ic, kbase, ke, lane, 64);
+      if (st < nsteps) produce_tile<NB, KF, VF>(tiles[wave], ic, kbase, ke, lane, 64, a.c);
       __syncthreads();
       if (st < nsteps) {
         half8_t kf[2][NB];
-        load_kfrag(kf, tiles[wave], lane);
-        group_step(gr, tiles[wave], kf, kbase, ke, a.c, lane);
+        float4_t kd[2][NB];
+        load_kfrag(kf, kd, tiles[wave], lane);
+        group_step(gr, tiles[wave], kf, kd, kbase, ke, lane);
       }
       __syncthreads();
     }
@@ -548,13 +584,14 @@ attention_kernel(AttnArgs a) {
   }
   for (int st = 0; st < nsteps; ++st) {
     const int kbase = kb + st * kStepKeys;
-    produce_tile<NB, KF, VF>(tiles[0], ic, kbase, ke, tid, kThreads);
+    produce_tile<NB, KF, VF>(tiles[0], ic, kbase, ke, tid, kThreads, a.c);
     __syncthreads();
     half8_t kf[2][NB];
-    load_kfrag(kf, tiles[0], lane);
+    float4_t kd[2][NB];
+    load_kfrag(kf, kd, tiles[0], lane);
 #pragma unroll
     for (int k = 0; k < kMaxGroupsPerWave; ++k)
-      if (wave + kWaves * k < ngroups) group_step(grs[k], tiles[0], kf, kbase, ke, a.c, lane);
+      if (wave + kWaves * k < ngroups) group_step(grs[k], tiles[0], kf, kd, kbase, ke, lane);
     __syncthreads();
   }
 #pragma unroll
