@@ -31,7 +31,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;       // attention work-group: 4 waves
 constexpr int kWaves = 4;
 constexpr int kStepKeys = 32;       // keys per LDS tile
-constexpr int kDecodeSplit = 512;   // keys per decode split (multiple of kStepKeys)
+constexpr int kDecodeSplit = 512;   // shortest decode split (multiple of kWaves*kStepKeys)
+constexpr int kMaxDecodeSplits = 64;
 constexpr int kChunkSplit = 32768;  // keys per chunk split (multiple of kStepKeys)
 constexpr int kChunkRows = 32;      // query rows per chunk tile
 constexpr int kMaxGroup = 8;        // query heads per KV head
@@ -47,17 +48,27 @@ __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; 
 
 // Work-item bookkeeping shared by host and device.  A sequence with more than
 // one row is a chunk: ceil(q_len/32) row tiles x Hkv x ceil(ctx/kChunkSplit)
-// key splits.  A one-row sequence is a decode row: Hkv x ceil(ctx/kDecodeSplit).
+// key splits.  A one-row sequence is a decode row: Hkv x ceil(ctx/split_len).
 struct SeqPlan {
-  int is_chunk, n_qt, n_split, items;
+  int is_chunk, n_qt, n_split, split_len, items;
 };
+
+// Keys per decode split: 512, doubled until the row has at most kMaxDecodeSplits
+// splits.  It depends only on the row's own context, so a row's arithmetic is
+// the same whatever else shares the batch.
+__host__ __device__ inline int decode_split_len(int ctx) {
+  int len = kDecodeSplit;
+  while ((int64_t)len * kMaxDecodeSplits < ctx) len *= 2;
+  return len;
+}
 
 __host__ __device__ inline SeqPlan plan_seq(int q_len, int prefix, int hkv) {
   SeqPlan p;
   const int ctx = prefix + q_len;
   p.is_chunk = q_len > 1;
   p.n_qt = p.is_chunk ? ceil_div(q_len, kChunkRows) : 1;
-  p.n_split = ceil_div(ctx, p.is_chunk ? kChunkSplit : kDecodeSplit);
+  p.split_len = p.is_chunk ? kChunkSplit : decode_split_len(ctx);
+  p.n_split = ceil_div(ctx, p.split_len);
   p.items = p.n_qt * hkv * p.n_split;
   return p;
 }
@@ -393,6 +404,212 @@ __device__ inline void load_kfrag(half8_t (&kf)[2][NB], float4_t (&kd)[2][NB], c
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode path: each wave streams raw blocks of its key range into a private
+// LDS stage (coalesced 16-byte loads, the next stage prefetched into
+// registers), and builds its MFMA operands straight from those bytes.
+// ---------------------------------------------------------------------------
+
+template <int NB, int KF, int VF>
+struct DecLayout {
+  static constexpr int kBK = Fmt<KF>::kBytes, kBV = Fmt<VF>::kBytes;
+  static constexpr int kRecK = NB * kBK, kRecV = NB * kBV;   // bytes per key of one KV head
+  static constexpr int kKBytes = kStepKeys * kRecK, kVBytes = kStepKeys * kRecV;
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = kKBytes + 16;                  // +16: over-read pad
+  static constexpr int kSKOff = kVOff + kVBytes + 16;         // float [NB][32]: K scale * c
+  static constexpr int kSVOff = kSKOff + NB * kStepKeys * 4;  // half  [NB][32]: V scale
+  static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
+  static constexpr int kChunksK = kKBytes / 16, kChunksV = kVBytes / 16;
+  static constexpr int kChunks = kChunksK + kChunksV;
+  static constexpr int kLoads = (kChunks + 63) / 64;
+  static_assert(kKBytes % 16 == 0 && kVBytes % 16 == 0 && kWaveBytes % 16 == 0, "alignment");
+};
+
+__device__ inline uint32_t lds_u32(const uint8_t* base, int off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+
+// 8 int8 codes starting at an even byte offset, as exact fp16 integers
+// (magic-number conversion: 0x6400|(c^0x80) is 1152 + c in fp16).
+__device__ inline half8_t lds_codes8_q8(const uint8_t* base, int off) {
+  const int a = off & ~3, sh = off & 3;
+  const uint32_t d0 = lds_u32(base, a), d1 = lds_u32(base, a + 4), d2 = lds_u32(base, a + 8);
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh) ^ 0x80808080u;
+  const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, sh) ^ 0x80808080u;
+  const half2_t bias = {(half_t)-1152.f, (half_t)-1152.f};
+  half2_t h[4];
+  h[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + bias;
+  h[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + bias;
+  h[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + bias;
+  h[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + bias;
+  return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+}
+
+// 8 two's-complement nibbles starting at an even byte offset, returned in the
+// element order (0,2,4,6,1,3,5,7) of the 8 values they encode.
+__device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
+  const int a = off & ~3, sh = off & 3;
+  const uint32_t d0 = lds_u32(base, a), d1 = lds_u32(base, a + 4);
+  const uint32_t w = __builtin_amdgcn_alignbyte(d1, d0, sh) ^ 0x88888888u;  // nibble + 8
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const half2_t bias = {(half_t)-1032.f, (half_t)-1032.f};
+  half2_t h[4];
+  h[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) + bias;
+  h[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) + bias;
+  h[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) + bias;
+  h[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) + bias;
+  return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+}
+
+// One value code of key record `rec` at value index `dv` within block b.
+template <int F>
+__device__ inline half_t lds_code1(const uint8_t* base, int rec_off, int dv) {
+  if constexpr (F == MAB_KV_Q8) {
+    return (half_t)(float)(int)(int8_t)base[rec_off + 2 + dv];
+  } else {
+    const int byte = base[rec_off + 2 + (dv >> 1)];
+    const int nib = (dv & 1) ? (byte >> 4) : (byte & 15);
+    return (half_t)(float)((nib ^ 8) - 8);
+  }
+}
+
+template <int NB, int KF, int VF>
+struct DecWave {
+  using L = DecLayout<NB, KF, VF>;
+  uint4 r[L::kLoads];  // the next stage's raw bytes, in flight
+
+  // Issue the loads of keys [kbase, kbase+32) of KV head c.g (two 16-key runs,
+  // each inside one page); runs at or past kend are not loaded.
+  __device__ inline void load(const ItemCtx& c, int kbase, int kend, int lane) {
+    const int ps = c.page_size;
+    int64_t runK[2], runV[2];
+    bool ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = kbase + 16 * h;
+      ok[h] = key < kend;
+      const int page = ok[h] ? c.bt_row[key / ps] : 0;
+      const int64_t tok = ((int64_t)page * c.hkv + c.g) * ps + key % ps;
+      runK[h] = tok * L::kRecK;
+      runV[h] = tok * L::kRecV;
+    }
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) {
+      const int ch = lane + 64 * i;
+      const uint8_t* src = nullptr;
+      if (ch < L::kChunksK) {
+        const int h = ch >= L::kRecK;
+        if (ok[h]) src = c.k_pool + runK[h] + (int64_t)(ch - h * L::kRecK) * 16;
+      } else if (ch < L::kChunks) {
+        const int cv = ch - L::kChunksK;
+        const int h = cv >= L::kRecV;
+        if (ok[h]) src = c.v_pool + runV[h] + (int64_t)(cv - h * L::kRecV) * 16;
+      }
+      r[i] = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Copy the stage into LDS and pull each block's scale into the compact
+  // scale arrays (a 16-byte chunk holds at most one scale: blocks are >= 18 B).
+  __device__ inline void store(uint8_t* w, int lane, float zc) {
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch >= L::kChunks) continue;
+      const bool isk = ch < L::kChunksK;
+      const int cc = isk ? ch : ch - L::kChunksK;
+      *reinterpret_cast<uint4*>(w + (isk ? L::kKOff : L::kVOff) + 16 * cc) = r[i];
+      const int bb = isk ? L::kBK : L::kBV;
+      const int m0 = (16 * cc + bb - 1) / bb;      // first block starting in this chunk
+      const int off = m0 * bb - 16 * cc;
+      if (off < 16) {
+        const uint32_t dw = off < 4 ? r[i].x : off < 8 ? r[i].y : off < 12 ? r[i].z : r[i].w;
+        const uint16_t bits = (uint16_t)(dw >> ((off & 2) * 8));
+        const int key = m0 / NB, b = m0 % NB;
+        if (isk) reinterpret_cast<float*>(w + L::kSKOff)[b * kStepKeys + key] =
+            (float)__builtin_bit_cast(half_t, bits) * zc;
+        else reinterpret_cast<uint16_t*>(w + L::kSVOff)[b * kStepKeys + key] = bits;
+      }
+    }
+  }
+};
+
+// One 32-key stage of a decode wave: S^T = K Q^T on integer codes per block,
+// fp32 block scales, online softmax, then O^T += V^T (P * V scale).
+template <int NB, int KF, int VF>
+__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, int lane) {
+  using L = DecLayout<NB, KF, VF>;
+  const int j = lane >> 4, n = lane & 15;
+  float4_t s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int rec = (16 * kt + n) * L::kRecK;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      half8_t kc;
+      if constexpr (KF == MAB_KV_Q8) kc = lds_codes8_q8(w + L::kKOff, rec + b * L::kBK + 2 + 8 * j);
+      else kc = lds_codes8_q4(w + L::kKOff, rec + b * L::kBK + 2 + 4 * j);
+      const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, gr.q[b], float4_t{0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0);
+      const float4_t kd = *reinterpret_cast<const float4_t*>(w + L::kSKOff + 4 * (b * kStepKeys + 16 * kt + 4 * j));
+      s[kt] += kd * pb;
+    }
+  }
+  float z[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kbase + 16 * kt + 4 * j + i;
+      z[kt][i] = (key < kend && key <= gr.limit) ? s[kt][i] : -INFINITY;
+      mx = fmaxf(mx, z[kt][i]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(gr.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(gr.m - m_use);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[4 * kt + i] = __builtin_amdgcn_exp2f(z[kt][i] - m_use);
+      psum += p[4 * kt + i];
+    }
+  gr.l = gr.l * alpha + psum;
+  gr.m = m_new;
+#pragma unroll
+  for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
+  const half_t* sv = reinterpret_cast<const half_t*>(w + L::kSVOff);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    // P operand for block b: keys 4j+[0,4) and 16+4j+[0,4), times their V scale
+    half8_t pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kk = (e < 4) ? 4 * j + e : 16 + 4 * j + (e - 4);
+      const bool ok = kbase + kk < kend;
+      pf[e] = ok ? (half_t)(p[e] * (float)sv[b * kStepKeys + kk]) : (half_t)0.f;
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int dv = 16 * t2 + n;  // value index inside block b
+      half8_t vc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e < 4) ? 4 * j + e : 16 + 4 * j + (e - 4);
+        vc[e] = lds_code1<VF>(w + L::kVOff, kk * L::kRecV + b * L::kBV, dv);
+      }
+      gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
+    }
+  }
+}
+
 struct AttnArgs {
   const half_t* q;
   const uint8_t* k_pool;
@@ -455,11 +672,31 @@ __device__ inline bool locate_item(const AttnArgs& a, int item, Found& f, int* s
   return f.s >= 0 && ctot == a.n_chunk_items;
 }
 
+template <int NB, int KF>
+__device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
+  group_init(gr, qrow, limit, lane);
+  if constexpr (KF == MAB_KV_Q4) {  // match the (0,2,4,6,1,3,5,7) order of 4-bit K codes
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const half8_t q = gr.q[b];
+      gr.q[b] = half8_t{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
+    }
+  }
+}
+
 template <int NB, int KF, int VF>
+constexpr int attn_smem_bytes(bool has_chunk) {
+  constexpr int dec = kWaves * DecLayout<NB, KF, VF>::kWaveBytes;
+  constexpr int merge = (kWaves * 16 * 32 * NB + 2 * kWaves * 16) * 4;
+  constexpr int base = dec > merge ? dec : merge;
+  return has_chunk && (int)sizeof(Tile<NB>) > base ? (int)sizeof(Tile<NB>) : base;
+}
+
+template <int NB, int KF, int VF, bool HAS_CHUNK>
 __global__ void __launch_bounds__(kThreads)
 attention_kernel(AttnArgs a) {
   constexpr int D = 32 * NB;
-  __shared__ Tile<NB> tiles[kWaves];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(HAS_CHUNK)];
   __shared__ int sh[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int item = blockIdx.x;
@@ -492,15 +729,13 @@ attention_kernel(AttnArgs a) {
     }
   }
 
-  const int split = p.is_chunk ? kChunkSplit : kDecodeSplit;
-  const int kb = j * split;
-  int ke = min(ctx, kb + split);
+  const int kb = j * p.split_len;
+  int ke = min(ctx, kb + p.split_len);
   if (p.is_chunk) {
     const int last_row = min(q_len, (qt + 1) * kChunkRows) - 1;
     ke = min(ke, prefix + last_row + 1);
     if (kb >= ke) return;  // no row of this tile sees this split
   }
-  const int nsteps = ceil_div(ke - kb, kStepKeys);
   const int64_t pbase = partial_base(item, a.n_chunk_items, G);
   const bool single = p.n_split == 1;
 
@@ -513,32 +748,34 @@ attention_kernel(AttnArgs a) {
   ic.page_size = a.page_size;
 
   if (!p.is_chunk) {
-    // Decode split: the four waves take interleaved 32-key steps, each with a
-    // private tile, then merge their softmax states in fixed wave order.
-    Group<NB> gr;
+    // Decode split: wave w streams keys [kb + w*len/4, kb + (w+1)*len/4) in
+    // 32-key stages; the waves then merge their softmax states in wave order.
+    using L = DecLayout<NB, KF, VF>;
+    uint8_t* wbuf = smem + wave * L::kWaveBytes;
     const int n = lane & 15;
-    const half_t* qrow = n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr;
-    group_init(gr, qrow, ctx - 1, lane);
-    for (int sb = 0; sb < nsteps; sb += kWaves) {
-      const int st = sb + wave;
-      const int kbase = kb + st * kStepKeys;
-      if (st < nsteps) produce_tile<NB, KF, VF>(tiles[wave], ic, kbase, ke, lane, 64, a.c);
-      __syncthreads();
-      if (st < nsteps) {
-        half8_t kf[2][NB];
-        float4_t kd[2][NB];
-        load_kfrag(kf, kd, tiles[wave], lane);
-        group_step(gr, tiles[wave], kf, kd, kbase, ke, lane);
-      }
-      __syncthreads();
+    Group<NB> gr;
+    dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
+    const int per_wave = p.split_len / kWaves;
+    const int kw0 = kb + wave * per_wave;
+    const int kw1 = min(ke, kw0 + per_wave);
+    const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
+    DecWave<NB, KF, VF> dw;
+    if (nst > 0) dw.load(ic, kw0, kw1, lane);
+    for (int st = 0; st < nst; ++st) {
+      const int kbase = kw0 + st * kStepKeys;
+      dw.store(wbuf, lane, a.c);
+      if (st + 1 < nst) dw.load(ic, kbase + kStepKeys, kw1, lane);
+      asm volatile("" ::: "memory");
+      dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, lane);
+      asm volatile("" ::: "memory");
     }
     float lsum = gr.l;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    // merge buffers alias the tiles (all reads of tiles are done)
-    float* mo = reinterpret_cast<float*>(&tiles[0]);     // [wave][16][D]
-    float* mm = mo + kWaves * 16 * D;                    // [wave][16]
-    float* ml = mm + kWaves * 16;                        // [wave][16]
+    __syncthreads();  // every wave is done with its stage buffer
+    float* mo = reinterpret_cast<float*>(smem);  // [wave][16][D]
+    float* mm = mo + kWaves * 16 * D;            // [wave][16]
+    float* ml = mm + kWaves * 16;                // [wave][16]
 #pragma unroll
     for (int tt = 0; tt < 2 * NB; ++tt)
 #pragma unroll
@@ -549,26 +786,31 @@ attention_kernel(AttnArgs a) {
       const int hl = u / D, dd = u % D;
       float M = -INFINITY;
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + hl]);
-      float L = 0.f, O = 0.f;
+      float Ls = 0.f, O = 0.f;
       for (int w = 0; w < kWaves; ++w) {
         const float sc = __builtin_amdgcn_exp2f(mm[w * 16 + hl] - M);
-        L += ml[w * 16 + hl] * sc;
+        Ls += ml[w * 16 + hl] * sc;
         O += mo[(w * 16 + hl) * D + dd] * sc;
       }
       const int h = g * G + hl;
       if (single) {
-        a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / L;
+        a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / Ls;
       } else {
         const int64_t pi = pbase + hl;
         if (pi < a.n_partials) {
           a.o_part[pi * D + dd] = O;
-          if (dd == 0) a.ml_part[pi] = make_float2(M, L);
+          if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
         }
       }
     }
     return;
   }
 
+  if constexpr (!HAS_CHUNK) {
+    return;
+  } else {
+  Tile<NB>* tiles = reinterpret_cast<Tile<NB>*>(smem);
+  const int nsteps = ceil_div(ke - kb, kStepKeys);
   // Chunk tile: 32 rows x G heads = 2G groups of 16 slots, dealt round-robin to
   // the four waves; all waves share one tile per step.
   Group<NB> grs[kMaxGroupsPerWave];
@@ -621,13 +863,18 @@ attention_kernel(AttnArgs a) {
       }
     }
   }
+  }  // HAS_CHUNK
 }
 
-// Merges the split-K partials of rows whose keys span several splits, in
-// ascending split order.  One work-group per row.
+// Merges the split-K partials of rows whose keys span several splits.  One
+// work-group per (row, query head): the max over splits is reduced across the
+// whole group, then each thread sums a strided subset of splits for one dim
+// and the subsets are added in fixed order, so the result is deterministic.
 __global__ void __launch_bounds__(256)
 combine_kernel(AttnArgs a, int head_dim) {
-  const int row = blockIdx.x;
+  __shared__ float red[2 * 256];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
   const int s = a.row_seq[row];
   if (s < 0 || s >= a.num_seqs) return;
   const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
@@ -637,32 +884,45 @@ combine_kernel(AttnArgs a, int head_dim) {
   const int G = a.hq / a.hkv;
   const int i = row - r0;
   if (i < 0 || i >= q_len || item_base < 0 || item_base >= a.n_items) return;
-  const int pos = prefix + i;
-  const int split = p.is_chunk ? kChunkSplit : kDecodeSplit;
-  const int nj = pos / split + 1;
+  const int nj = (prefix + i) / p.split_len + 1;
   const int qt = i / kChunkRows, rr = i % kChunkRows;
-  for (int u = threadIdx.x; u < a.hq * head_dim; u += blockDim.x) {
-    const int h = u / head_dim, dd = u % head_dim;
-    const int g = h / G, hl = h % G;
-    float M = -INFINITY;
-    for (int j = 0; j < nj; ++j) {
-      const int item = p.is_chunk ? item_base + qt + p.n_qt * (j + p.n_split * g)
-                                  : item_base + g * p.n_split + j;
-      const int64_t pi = partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
-      if (pi >= a.n_partials) return;
-      M = fmaxf(M, a.ml_part[pi].x);
+  const int g = h / G, hl = h % G;
+  auto pidx = [&](int jj) -> int64_t {
+    const int item = p.is_chunk ? item_base + qt + p.n_qt * (jj + p.n_split * g) : item_base + g * p.n_split + jj;
+    return partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
+  };
+  float M = -INFINITY;
+  for (int jj = tid; jj < nj; jj += blockDim.x) {
+    const int64_t pi = pidx(jj);
+    if (pi >= 0 && pi < a.n_partials) M = fmaxf(M, a.ml_part[pi].x);
+  }
+  red[tid] = M;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  const int sgs = blockDim.x / head_dim, d = tid % head_dim, sg = tid / head_dim;
+  float O = 0.f, Ls = 0.f;
+  for (int jj = sg; jj < nj; jj += sgs) {
+    const int64_t pi = pidx(jj);
+    if (pi < 0 || pi >= a.n_partials) continue;
+    const float2 ml = a.ml_part[pi];
+    const float sc = __builtin_amdgcn_exp2f(ml.x - M);
+    Ls += ml.y * sc;
+    O += a.o_part[pi * head_dim + d] * sc;
+  }
+  red[tid] = O;
+  red[256 + tid] = Ls;
+  __syncthreads();
+  if (sg == 0) {
+    for (int k = 1; k < sgs; ++k) {
+      O += red[k * head_dim + d];
+      Ls += red[256 + k * head_dim + d];
     }
-    float L = 0.f, O = 0.f;
-    for (int j = 0; j < nj; ++j) {
-      const int item = p.is_chunk ? item_base + qt + p.n_qt * (j + p.n_split * g)
-                                  : item_base + g * p.n_split + j;
-      const int64_t pi = partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
-      const float2 ml = a.ml_part[pi];
-      const float sc = __builtin_amdgcn_exp2f(ml.x - M);
-      L += ml.y * sc;
-      O += a.o_part[pi * head_dim + dd] * sc;
-    }
-    a.out[((int64_t)row * a.hq + h) * head_dim + dd] = O / L;
+    a.out[((int64_t)row * a.hq + h) * head_dim + d] = O / Ls;
   }
 }
 
@@ -729,7 +989,10 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 
 template <int NB, int KF, int VF>
 void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
+  if (a.n_chunk_items > 0)
+    hipLaunchKernelGGL((attention_kernel<NB, KF, VF, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<NB, KF, VF, false>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
 template <int NB>
@@ -827,7 +1090,8 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
   else launch_attention_nb<4>(layout, a, grid, hs);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows), dim3(256), 0, hs, a, layout->head_dim);
+  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows * layout->num_q_heads), dim3(256), 0, hs, a,
+                     layout->head_dim);
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
 
