@@ -27,12 +27,14 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
 constexpr int kThreads = 256;       // attention work-group: 4 waves
 constexpr int kWaves = 4;
 constexpr int kStepKeys = 32;       // keys per LDS tile
-constexpr int kDecodeSplit = 512;   // shortest decode split (multiple of kWaves*kStepKeys)
-constexpr int kMaxDecodeSplits = 64;
+constexpr int kDecodeSplit = 2048;  // shortest decode split (multiple of kWaves*kStepKeys)
+constexpr int kMaxDecodeSplit = 4096;  // longest decode split: 1024 keys (64 runs of 16) per wave
+constexpr int kMaxDecodeSplits = 128;
 constexpr int kChunkSplit = 32768;  // keys per chunk split (multiple of kStepKeys)
 constexpr int kChunkRows = 32;      // query rows per chunk tile
 constexpr int kMaxGroup = 8;        // query heads per KV head
@@ -53,12 +55,12 @@ struct SeqPlan {
   int is_chunk, n_qt, n_split, split_len, items;
 };
 
-// Keys per decode split: 512, doubled until the row has at most kMaxDecodeSplits
-// splits.  It depends only on the row's own context, so a row's arithmetic is
+// Keys per decode split: kDecodeSplit, doubled (up to kMaxDecodeSplit) until
+// the row has at most kMaxDecodeSplits splits.  It depends only on the row's own context, so a row's arithmetic is
 // the same whatever else shares the batch.
 __host__ __device__ inline int decode_split_len(int ctx) {
   int len = kDecodeSplit;
-  while ((int64_t)len * kMaxDecodeSplits < ctx) len *= 2;
+  while ((int64_t)len * kMaxDecodeSplits < ctx && len < kMaxDecodeSplit) len *= 2;
   return len;
 }
 
@@ -415,14 +417,15 @@ struct DecLayout {
   static constexpr int kBK = Fmt<KF>::kBytes, kBV = Fmt<VF>::kBytes;
   static constexpr int kRecK = NB * kBK, kRecV = NB * kBV;   // bytes per key of one KV head
   static constexpr int kKBytes = kStepKeys * kRecK, kVBytes = kStepKeys * kRecV;
-  static constexpr int kKOff = 0;
-  static constexpr int kVOff = kKBytes + 16;                  // +16: over-read pad
-  static constexpr int kSKOff = kVOff + kVBytes + 16;         // float [NB][32]: K scale * c
-  static constexpr int kSVOff = kSKOff + NB * kStepKeys * 4;  // half  [NB][32]: V scale
-  static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
   static constexpr int kChunksK = kKBytes / 16, kChunksV = kVBytes / 16;
   static constexpr int kChunks = kChunksK + kChunksV;
-  static constexpr int kLoads = (kChunks + 63) / 64;
+  static constexpr int kLoads = (kChunks + 63) / 64;          // 16-byte loads per lane per stage
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = kKBytes;
+  static constexpr int kRawBytes = kLoads * 1024 + 16;        // tail lanes + over-read pad
+  static constexpr int kSKOff = kRawBytes;                    // float [NB][32]: K scale * c
+  static constexpr int kSVOff = kSKOff + NB * kStepKeys * 4;  // half  [NB][32]: V scale
+  static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
   static_assert(kKBytes % 16 == 0 && kVBytes % 16 == 0 && kWaveBytes % 16 == 0, "alignment");
 };
 
@@ -462,78 +465,86 @@ __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
   return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
 }
 
-// One value code of key record `rec` at value index `dv` within block b.
+// Codes of value index dv (within block) for two keys at byte offsets o0, o1 of
+// their block payloads, as an fp16 pair of exact integers.
 template <int F>
-__device__ inline half_t lds_code1(const uint8_t* base, int rec_off, int dv) {
+__device__ inline half2_t lds_code_pair(const uint8_t* base, int o0, int o1, int dv) {
   if constexpr (F == MAB_KV_Q8) {
-    return (half_t)(float)(int)(int8_t)base[rec_off + 2 + dv];
+    const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
+    const half2_t bias = {(half_t)-1152.f, (half_t)-1152.f};
+    return __builtin_bit_cast(half2_t, w ^ 0x64806480u) + bias;
   } else {
-    const int byte = base[rec_off + 2 + (dv >> 1)];
-    const int nib = (dv & 1) ? (byte >> 4) : (byte & 15);
-    return (half_t)(float)((nib ^ 8) - 8);
+    uint32_t w = (uint32_t)base[o0 + (dv >> 1)] | ((uint32_t)base[o1 + (dv >> 1)] << 16);
+    w = ((dv & 1) ? (w >> 4) : w) & 0x000F000Fu;
+    const half2_t bias = {(half_t)-1032.f, (half_t)-1032.f};
+    return __builtin_bit_cast(half2_t, w ^ 0x64086408u) + bias;
   }
 }
 
 template <int NB, int KF, int VF>
 struct DecWave {
   using L = DecLayout<NB, KF, VF>;
-  uint4 r[L::kLoads];  // the next stage's raw bytes, in flight
+  u32x4_t r[L::kLoads];  // the next stage's raw bytes, in flight
 
-  // Issue the loads of keys [kbase, kbase+32) of KV head c.g (two 16-key runs,
-  // each inside one page); runs at or past kend are not loaded.
-  __device__ inline void load(const ItemCtx& c, int kbase, int kend, int lane) {
+  // Issue the loads of keys [kbase, kbase+32) of KV head c.g: two 16-key runs,
+  // each inside one page (ids page0, page1).  A run at or past kend re-reads
+  // run 0 instead (its keys are masked), and lanes past the last chunk re-read
+  // the last chunk, so every lane loads valid memory without branching.
+  __device__ __attribute__((always_inline)) void load(const ItemCtx& c, int kbase, int kend, int page0, int page1, int lane) {
     const int ps = c.page_size;
-    int64_t runK[2], runV[2];
-    bool ok[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = kbase + 16 * h;
-      ok[h] = key < kend;
-      const int page = ok[h] ? c.bt_row[key / ps] : 0;
-      const int64_t tok = ((int64_t)page * c.hkv + c.g) * ps + key % ps;
-      runK[h] = tok * L::kRecK;
-      runV[h] = tok * L::kRecV;
-    }
-#pragma unroll
+    const int key1 = kbase + 16;
+    const int64_t tok0 = ((int64_t)page0 * c.hkv + c.g) * ps + kbase % ps;
+    const int64_t tok1 = key1 < kend ? ((int64_t)page1 * c.hkv + c.g) * ps + key1 % ps : tok0;
+    const uint8_t* k0 = c.k_pool + tok0 * L::kRecK;
+    const uint8_t* k1 = c.k_pool + tok1 * L::kRecK;
+    const uint8_t* v0 = c.v_pool + tok0 * L::kRecV;
+    const uint8_t* v1 = c.v_pool + tok1 * L::kRecV;
+#pragma clang loop unroll(full)
     for (int i = 0; i < L::kLoads; ++i) {
       const int ch = lane + 64 * i;
-      const uint8_t* src = nullptr;
-      if (ch < L::kChunksK) {
-        const int h = ch >= L::kRecK;
-        if (ok[h]) src = c.k_pool + runK[h] + (int64_t)(ch - h * L::kRecK) * 16;
-      } else if (ch < L::kChunks) {
+      const uint8_t* src;
+      if (64 * i + 63 < L::kChunksK) {          // all lanes in the K region
+        src = ch < L::kRecK ? k0 + 16 * ch : k1 + 16 * (ch - L::kRecK);
+      } else if (64 * i >= L::kChunksK) {       // all lanes in the V region
+        const int cv = min(ch - L::kChunksK, L::kChunksV - 1);
+        src = cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
+      } else {                                  // the boundary load
         const int cv = ch - L::kChunksK;
-        const int h = cv >= L::kRecV;
-        if (ok[h]) src = c.v_pool + runV[h] + (int64_t)(cv - h * L::kRecV) * 16;
+        src = ch < L::kRecK ? k0 + 16 * ch
+            : ch < L::kChunksK ? k1 + 16 * (ch - L::kRecK)
+            : cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
       }
-      r[i] = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+      r[i] = *reinterpret_cast<const u32x4_t*>(src);
     }
   }
 
-  // Copy the stage into LDS and pull each block's scale into the compact
-  // scale arrays (a 16-byte chunk holds at most one scale: blocks are >= 18 B).
-  __device__ inline void store(uint8_t* w, int lane, float zc) {
-#pragma unroll
-    for (int i = 0; i < L::kLoads; ++i) {
-      const int ch = lane + 64 * i;
-      if (ch >= L::kChunks) continue;
-      const bool isk = ch < L::kChunksK;
-      const int cc = isk ? ch : ch - L::kChunksK;
-      *reinterpret_cast<uint4*>(w + (isk ? L::kKOff : L::kVOff) + 16 * cc) = r[i];
-      const int bb = isk ? L::kBK : L::kBV;
-      const int m0 = (16 * cc + bb - 1) / bb;      // first block starting in this chunk
-      const int off = m0 * bb - 16 * cc;
-      if (off < 16) {
-        const uint32_t dw = off < 4 ? r[i].x : off < 8 ? r[i].y : off < 12 ? r[i].z : r[i].w;
-        const uint16_t bits = (uint16_t)(dw >> ((off & 2) * 8));
-        const int key = m0 / NB, b = m0 % NB;
-        if (isk) reinterpret_cast<float*>(w + L::kSKOff)[b * kStepKeys + key] =
-            (float)__builtin_bit_cast(half_t, bits) * zc;
-        else reinterpret_cast<uint16_t*>(w + L::kSVOff)[b * kStepKeys + key] = bits;
-      }
-    }
+  // Copy the stage into LDS (lanes past the last chunk land in the tail pad).
+  __device__ __attribute__((always_inline)) void store(uint8_t* w, int lane) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < L::kLoads; ++i) *reinterpret_cast<u32x4_t*>(w + 16 * (lane + 64 * i)) = r[i];
   }
 };
+
+// Pulls the K and V block scales of the stage in LDS into the compact arrays:
+// K scales as fp32 times c = sm_scale*log2(e), V scales as fp16, both [block][key].
+template <int NB, int KF, int VF>
+__device__ inline void dec_scales(uint8_t* w, int lane, float zc) {
+  using L = DecLayout<NB, KF, VF>;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    const int idx = lane + 64 * q;            // NB*64 = 2*32*NB entries: K first, then V
+    const bool isv = q >= NB / 2;
+    const int m = isv ? idx - 32 * NB : idx;
+    const int b = m / kStepKeys, key = m % kStepKeys;
+    if (!isv) {
+      const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kKOff + key * L::kRecK + b * L::kBK);
+      reinterpret_cast<float*>(w + L::kSKOff)[m] = (float)__builtin_bit_cast(half_t, bits) * zc;
+    } else {
+      const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
+      reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = bits;
+    }
+  }
+}
 
 // One 32-key stage of a decode wave: S^T = K Q^T on integer codes per block,
 // fp32 block scales, online softmax, then O^T += V^T (P * V scale).
@@ -557,15 +568,15 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
       s[kt] += kd * pb;
     }
   }
-  float z[2][4];
+  float z[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = kbase + 16 * kt + 4 * j + i;
-      z[kt][i] = (key < kend && key <= gr.limit) ? s[kt][i] : -INFINITY;
-      mx = fmaxf(mx, z[kt][i]);
+      z[4 * kt + i] = (key < kend && key <= gr.limit) ? s[kt][i] : -INFINITY;
+      mx = fmaxf(mx, z[4 * kt + i]);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -575,36 +586,41 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
   float p[8];
   float psum = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[4 * kt + i] = __builtin_amdgcn_exp2f(z[kt][i] - m_use);
-      psum += p[4 * kt + i];
-    }
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(z[e] - m_use);  // masked keys: exactly 0
+    psum += p[e];
+  }
   gr.l = gr.l * alpha + psum;
   gr.m = m_new;
 #pragma unroll
   for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
+  // keys of this lane's P operand: 4j+[0,4) and 16+4j+[0,4); V scales of keys
+  // past kend may be garbage (even NaN), so their P' is forced to 0.
+  bool ok[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ok[e] = kbase + ((e < 4) ? 4 * j + e : 12 + 4 * j + e) < kend;
   const half_t* sv = reinterpret_cast<const half_t*>(w + L::kSVOff);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    // P operand for block b: keys 4j+[0,4) and 16+4j+[0,4), times their V scale
+    const half4_t s0 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 4 * j);
+    const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
     half8_t pf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kk = (e < 4) ? 4 * j + e : 16 + 4 * j + (e - 4);
-      const bool ok = kbase + kk < kend;
-      pf[e] = ok ? (half_t)(p[e] * (float)sv[b * kStepKeys + kk]) : (half_t)0.f;
+    for (int e = 0; e < 4; ++e) {
+      pf[e] = ok[e] ? (half_t)(p[e] * (float)s0[e]) : (half_t)0.f;
+      pf[4 + e] = ok[4 + e] ? (half_t)(p[4 + e] * (float)s1[e]) : (half_t)0.f;
     }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int dv = 16 * t2 + n;  // value index inside block b
-      half8_t vc;
+      half2_t vp[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = (e < 4) ? 4 * j + e : 16 + 4 * j + (e - 4);
-        vc[e] = lds_code1<VF>(w + L::kVOff, kk * L::kRecV + b * L::kBV, dv);
+      for (int e = 0; e < 4; ++e) {
+        const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
+        vp[e] = lds_code_pair<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + 2,
+                                  (ka + 1) * L::kRecV + b * L::kBV + 2, dv);
       }
+      const half8_t vc = half8_t{vp[0][0], vp[0][1], vp[1][0], vp[1][1], vp[2][0], vp[2][1], vp[3][0], vp[3][1]};
       gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
     }
   }
@@ -693,11 +709,8 @@ constexpr int attn_smem_bytes(bool has_chunk) {
 }
 
 template <int NB, int KF, int VF, bool HAS_CHUNK>
-__global__ void __launch_bounds__(kThreads)
-attention_kernel(AttnArgs a) {
+__device__ inline void attention_body(const AttnArgs& a, uint8_t* smem, int* sh) {
   constexpr int D = 32 * NB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(HAS_CHUNK)];
-  __shared__ int sh[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int item = blockIdx.x;
 
@@ -759,12 +772,20 @@ attention_kernel(AttnArgs a) {
     const int kw0 = kb + wave * per_wave;
     const int kw1 = min(ke, kw0 + per_wave);
     const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
+    // page ids of the wave's 16-key runs (at most 64), one per lane
+    const int nruns = ceil_div(max(kw1 - kw0, 0), 16);
+    const int my_page = lane < nruns ? ic.bt_row[(kw0 + 16 * lane) / a.page_size] : 0;
     DecWave<NB, KF, VF> dw;
-    if (nst > 0) dw.load(ic, kw0, kw1, lane);
+    if (nst > 0)
+      dw.load(ic, kw0, kw1, __builtin_amdgcn_readlane(my_page, 0), __builtin_amdgcn_readlane(my_page, 1), lane);
     for (int st = 0; st < nst; ++st) {
       const int kbase = kw0 + st * kStepKeys;
-      dw.store(wbuf, lane, a.c);
-      if (st + 1 < nst) dw.load(ic, kbase + kStepKeys, kw1, lane);
+      dw.store(wbuf, lane);
+      asm volatile("" ::: "memory");
+      dec_scales<NB, KF, VF>(wbuf, lane, a.c);
+      if (st + 1 < nst)
+        dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, 2 * st + 2),
+                __builtin_amdgcn_readlane(my_page, 2 * st + 3), lane);
       asm volatile("" ::: "memory");
       dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, lane);
       asm volatile("" ::: "memory");
@@ -866,13 +887,33 @@ attention_kernel(AttnArgs a) {
   }  // HAS_CHUNK
 }
 
+// Batches with a chunk: heavy chunk tiles and decode splits in one launch.
+template <int NB, int KF, int VF>
+__global__ void __launch_bounds__(kThreads)
+mixed_attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(true)];
+  __shared__ int sh[16];
+  attention_body<NB, KF, VF, true>(a, smem, sh);
+}
+
+// Decode-only batches: the same decode splits, compiled for at least three waves per SIMD.
+template <int NB, int KF, int VF>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+decode_attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(false)];
+  __shared__ int sh[16];
+  attention_body<NB, KF, VF, false>(a, smem, sh);
+}
+
 // Merges the split-K partials of rows whose keys span several splits.  One
 // work-group per (row, query head): the max over splits is reduced across the
 // whole group, then each thread sums a strided subset of splits for one dim
 // and the subsets are added in fixed order, so the result is deterministic.
-__global__ void __launch_bounds__(256)
+constexpr int kCombineThreads = 1024;
+
+__global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(AttnArgs a, int head_dim) {
-  __shared__ float red[2 * 256];
+  __shared__ float red[2 * kCombineThreads];
   const int tid = threadIdx.x;
   const int row = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
   const int s = a.row_seq[row];
@@ -915,12 +956,12 @@ combine_kernel(AttnArgs a, int head_dim) {
     O += a.o_part[pi * head_dim + d] * sc;
   }
   red[tid] = O;
-  red[256 + tid] = Ls;
+  red[kCombineThreads + tid] = Ls;
   __syncthreads();
   if (sg == 0) {
     for (int k = 1; k < sgs; ++k) {
       O += red[k * head_dim + d];
-      Ls += red[256 + k * head_dim + d];
+      Ls += red[kCombineThreads + k * head_dim + d];
     }
     a.out[((int64_t)row * a.hq + h) * head_dim + d] = O / Ls;
   }
@@ -990,9 +1031,9 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 template <int NB, int KF, int VF>
 void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((attention_kernel<NB, KF, VF, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attention_kernel<NB, KF, VF, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
 template <int NB>
@@ -1090,8 +1131,8 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
   else launch_attention_nb<4>(layout, a, grid, hs);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows * layout->num_q_heads), dim3(256), 0, hs, a,
-                     layout->head_dim);
+  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows * layout->num_q_heads), dim3(kCombineThreads), 0,
+                     hs, a, layout->head_dim);
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
 

@@ -66,15 +66,15 @@ def test_workspace_closed_form():
     lay = mab.make_layout(24, 4, 128, 256, 1000)
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
-    # decode items: 4 heads x ceil(ctx/len), len = 512 doubled until ctx <= 64*len;
+    # decode items: 4 heads x ceil(ctx/len), len = 2048 doubled (up to 4096) while 128*len < ctx;
     # chunk: 2 tiles x 4 heads x 1 split, 32 rows x 6 heads each
     def split_len(ctx):
-        n = 512
-        while 64 * n < ctx:
+        n = 2048
+        while 128 * n < ctx and n < 4096:
             n *= 2
         return n
-    assert split_len(1001) == 512 and split_len(70001) == 2048
-    dec_items = 4 * (-(-1001 // 512)) + 4 * (-(-70001 // 2048))
+    assert split_len(1001) == 2048 and split_len(70001) == 2048 and split_len(300000) == 4096
+    dec_items = 4 * (-(-1001 // 2048)) + 4 * (-(-70001 // 2048))
     chunk_items = 2 * 4 * 1
     partials = chunk_items * 6 * 32 + dec_items * 6
     assert n >= partials * (128 + 2) * 4
