@@ -7,14 +7,15 @@
 //                 (8-bit codes) or 18 bytes (4-bit codes), bit-exact codec.
 //
 // Kernels:
-//   append_kernel     -- encode new K/V rows into blocks at their page slots.
-//   attention_kernel  -- one launch over a flat list of work items: chunk
-//                        tiles first (heavy), then decode splits.  Each item
-//                        dequantizes its KV tiles into LDS as fp16, runs
-//                        S^T = K Q^T and O^T = V^T P^T on 16x16x32 fp16 MFMA
-//                        with fp32 accumulation and an fp32 online softmax.
-//   combine_kernel    -- log-sum-exp merge of split-K partials, ascending
-//                        split order, for rows whose keys span several splits.
+//   append_kernel           -- encode new K/V rows into blocks at their page slots.
+//   mixed_attention_kernel  -- one launch over a flat list of work items: chunk
+//                              tiles first (heavy), then decode splits.
+//   decode_attention_kernel -- the same decode splits for batches without a chunk.
+//   combine_kernel          -- log-sum-exp merge of split-K partials in fixed order.
+// Decode splits stream raw blocks per wave and build 16x16x32 MFMA operands from
+// the bytes; chunk tiles dequantize each 32-key step once into a shared LDS tile
+// and run 32x32x16 MFMAs.  Keys always enter the MFMA as exact integer codes with
+// their block scale applied in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,20 +28,20 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
-constexpr int kThreads = 256;       // attention work-group: 4 waves
-constexpr int kWaves = 4;
-constexpr int kStepKeys = 32;       // keys per LDS tile
-constexpr int kDecodeSplit = 2048;  // shortest decode split (multiple of kWaves*kStepKeys)
-constexpr int kMaxDecodeSplit = 4096;  // longest decode split: 1024 keys (64 runs of 16) per wave
+constexpr int kDecodeWaves = 4;     // waves that stream a decode split (in either kernel)
+constexpr int kMaxWaves = 8;        // waves of a mixed work-group (G * ceil(4/G) <= 8)
+constexpr int kStepKeys = 32;       // keys per stage / tile
+constexpr int kDecodeSplit = 2048;  // shortest decode split (multiple of kMaxWaves*kStepKeys)
+constexpr int kMaxDecodeSplit = 4096;  // longest decode split: at most 64 16-key runs per wave
 constexpr int kMaxDecodeSplits = 128;
-constexpr int kChunkSplit = 32768;  // keys per chunk split (multiple of kStepKeys)
-constexpr int kChunkRows = 32;      // query rows per chunk tile
+constexpr int kChunkSplit = 65536;  // keys per chunk split (multiple of kStepKeys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
-constexpr int kMaxGroupsPerWave = 4;  // 16-slot query groups per wave (chunk)
 constexpr int kMaxSeqs = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
 
 template <int F> struct Fmt;
 template <> struct Fmt<MAB_KV_Q8> { static constexpr int kBytes = 34; static constexpr int kQmax = 127; };
@@ -48,36 +49,42 @@ template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static con
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Waves of a mixed work-group and rows of a chunk tile: every wave of a chunk
+// tile serves one query head of the group and 32 rows, so a tile has
+// 32*ceil(4/G) rows and G*ceil(4/G) waves (at least four waves per group).
+__host__ __device__ inline int mixed_waves(int group) { return group * ceil_div(4, group); }
+__host__ __device__ inline int chunk_rows(int group) { return 32 * ceil_div(4, group); }
+
 // Work-item bookkeeping shared by host and device.  A sequence with more than
-// one row is a chunk: ceil(q_len/32) row tiles x Hkv x ceil(ctx/kChunkSplit)
+// one row is a chunk: ceil(q_len/rows) row tiles x Hkv x ceil(ctx/kChunkSplit)
 // key splits.  A one-row sequence is a decode row: Hkv x ceil(ctx/split_len).
 struct SeqPlan {
   int is_chunk, n_qt, n_split, split_len, items;
 };
 
 // Keys per decode split: kDecodeSplit, doubled (up to kMaxDecodeSplit) until
-// the row has at most kMaxDecodeSplits splits.  It depends only on the row's own context, so a row's arithmetic is
-// the same whatever else shares the batch.
+// the row has at most kMaxDecodeSplits splits.  It depends only on the row's
+// own context, so a row's arithmetic is the same whatever shares the batch.
 __host__ __device__ inline int decode_split_len(int ctx) {
   int len = kDecodeSplit;
   while ((int64_t)len * kMaxDecodeSplits < ctx && len < kMaxDecodeSplit) len *= 2;
   return len;
 }
 
-__host__ __device__ inline SeqPlan plan_seq(int q_len, int prefix, int hkv) {
+__host__ __device__ inline SeqPlan plan_seq(int q_len, int prefix, int hkv, int group) {
   SeqPlan p;
   const int ctx = prefix + q_len;
   p.is_chunk = q_len > 1;
-  p.n_qt = p.is_chunk ? ceil_div(q_len, kChunkRows) : 1;
+  p.n_qt = p.is_chunk ? ceil_div(q_len, chunk_rows(group)) : 1;
   p.split_len = p.is_chunk ? kChunkSplit : decode_split_len(ctx);
   p.n_split = ceil_div(ctx, p.split_len);
   p.items = p.n_qt * hkv * p.n_split;
   return p;
 }
 
-// Partial-result slots: chunk items own G*32 slots, decode items own G slots.
+// Partial-result slots: a chunk item owns G*rows slots, a decode item G slots.
 __host__ __device__ inline int64_t partial_base(int64_t item, int64_t n_chunk_items, int group) {
-  const int64_t cs = (int64_t)group * kChunkRows;
+  const int64_t cs = (int64_t)group * chunk_rows(group);
   return item < n_chunk_items ? item * cs : n_chunk_items * cs + (item - n_chunk_items) * group;
 }
 
@@ -182,69 +189,8 @@ append_kernel(const half_t* __restrict__ k_new, const half_t* __restrict__ v_new
 }
 
 // ---------------------------------------------------------------------------
-// Attention
+// Attention: shared pieces
 // ---------------------------------------------------------------------------
-
-// Reads the byte-aligned 8 codes (or 4 bytes of nibbles) of a block through
-// 16-bit loads: blocks are 34 or 18 bytes long, so they only start on even
-// byte addresses.
-__device__ inline uint32_t load_u32_even(const uint8_t* p) {
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-  return (uint32_t)q[0] | ((uint32_t)q[1] << 16);
-}
-
-// Codes 8j .. 8j+7 of the block at blk as exact fp16 integers (no scale).
-template <int F>
-__device__ inline void codes8(const uint8_t* blk, int j, half_t out[8]) {
-  if constexpr (F == MAB_KV_Q8) {
-    const uint32_t w0 = load_u32_even(blk + 2 + 8 * j);
-    const uint32_t w1 = load_u32_even(blk + 2 + 8 * j + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[e] = (half_t)(float)(int8_t)(w0 >> (8 * e));
-      out[4 + e] = (half_t)(float)(int8_t)(w1 >> (8 * e));
-    }
-  } else {
-    const uint32_t w = load_u32_even(blk + 2 + 4 * j);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int nib = (int)((w >> (4 * e)) & 0xF);
-      out[e] = (half_t)(float)(nib >= 8 ? nib - 16 : nib);
-    }
-  }
-}
-
-template <int F>
-__device__ inline void dequant8(const uint8_t* blk, int j, half_t out[8]) {
-  // values 8j .. 8j+7 of the block at blk, as fp16(code * d)
-  const half_t d = __builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(blk));
-  if constexpr (F == MAB_KV_Q8) {
-    const uint32_t w0 = load_u32_even(blk + 2 + 8 * j);
-    const uint32_t w1 = load_u32_even(blk + 2 + 8 * j + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[e] = (half_t)(float)(int8_t)(w0 >> (8 * e)) * d;
-      out[4 + e] = (half_t)(float)(int8_t)(w1 >> (8 * e)) * d;
-    }
-  } else {
-    const uint32_t w = load_u32_even(blk + 2 + 4 * j);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int nib = (int)((w >> (4 * e)) & 0xF);
-      out[e] = (half_t)(float)(nib >= 8 ? nib - 16 : nib) * d;
-    }
-  }
-}
-
-template <int NB>
-struct Tile {
-  static constexpr int kD = 32 * NB;
-  static constexpr int kKStride = kD + 8;         // halves per K row (16-byte rows, skewed)
-  static constexpr int kVStride = kStepKeys + 8;  // halves per V^T row
-  half_t k[kStepKeys * kKStride];                 // K codes [key][dim], exact fp16 integers
-  half_t vt[kD * kVStride];                       // V_hat^T [dim][key]
-  float kd[NB * kStepKeys];                       // K scale * sm_scale * log2(e), [block][key]
-};
 
 struct ItemCtx {
   const uint8_t* k_pool;
@@ -253,66 +199,9 @@ struct ItemCtx {
   int hkv, g, page_size;
 };
 
-// Dequantize keys [kbase, kbase+32) of KV head g into tile t; keys >= kend are zero.
-// Executed by threads [0, nthr) of the caller's set (index `tid`).
-template <int NB, int KF, int VF>
-__device__ inline void produce_tile(Tile<NB>& t, const ItemCtx& c, int kbase, int kend, int tid, int nthr,
-                                    float zc) {
-  constexpr int D = 32 * NB;
-  constexpr int KB = Fmt<KF>::kBytes, VB = Fmt<VF>::kBytes;
-  // K: unit = (key, block b, 8-value group j)
-  for (int u = tid; u < kStepKeys * NB * 4; u += nthr) {
-    const int kk = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
-    const int key = kbase + kk;
-    half_t v[8];
-    float kd = 0.f;
-    if (key < kend) {
-      const int page = c.bt_row[key / c.page_size];
-      const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + key % c.page_size;
-      const uint8_t* blk = c.k_pool + (tok * NB + b) * KB;
-      codes8<KF>(blk, j, v);
-      kd = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(blk)) * zc;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (half_t)0.f;
-    }
-    if (j == 0) t.kd[b * kStepKeys + kk] = kd;
-    half8_t h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = v[e];
-    *reinterpret_cast<half8_t*>(&t.k[kk * Tile<NB>::kKStride + 32 * b + 8 * j]) = h;
-  }
-  // V^T: unit = (key pair, block b, 8-value group j)
-  for (int u = tid; u < (kStepKeys / 2) * NB * 4; u += nthr) {
-    const int kp = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
-    half_t v0[8], v1[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = kbase + 2 * kp + h;
-      half_t* v = h ? v1 : v0;
-      if (key < kend) {
-        const int page = c.bt_row[key / c.page_size];
-        const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + key % c.page_size;
-        dequant8<VF>(c.v_pool + (tok * NB + b) * VB, j, v);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (half_t)0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      half2_t pr;
-      pr[0] = v0[e];
-      pr[1] = v1[e];
-      *reinterpret_cast<half2_t*>(&t.vt[(32 * b + 8 * j + e) * Tile<NB>::kVStride + 2 * kp]) = pr;
-    }
-  }
-  (void)D;
-}
-
-// Online-softmax state of one 16-slot query group held by one wave.
-// Lane l serves slot l%16; the four lanes of a slot hold different keys of S^T
-// and different dims of O^T.
+// Online-softmax state of one decode wave.  The 16 MFMA slots are the G query
+// heads of the KV head; lane l serves slot l%16, and the four lanes of a slot
+// hold different keys of S^T and different dims of O^T.
 template <int NB>
 struct Group {
   half8_t q[NB];          // Q^T operand: slot l%16, dims 32b + 8(l/16) + [0,8)
@@ -335,81 +224,21 @@ __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, 
   gr.limit = qrow ? limit : -1;
 }
 
-// One 32-key step of one group against tile t.
-// Scores: one MFMA per 32-dim block on the exact integer codes, then the
-// block's scale (already multiplied by sm_scale*log2(e)) applied in fp32, so
-// the only roundings are fp32 ones.
-template <int NB>
-__device__ inline void group_step(Group<NB>& gr, const Tile<NB>& t, const half8_t (&kf)[2][NB],
-                                  const float4_t (&kd)[2][NB], int kbase, int kend, int lane) {
-  float4_t s[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kt][b], gr.q[b],
-                                                                 float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      s[kt] += kd[kt][b] * pb;
-    }
-  }
-  // scores in log2 units, masked by position
-  float z[2][4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kbase + 16 * kt + 4 * (lane >> 4) + i;
-      const bool ok = key <= gr.limit && key < kend;
-      z[kt][i] = ok ? s[kt][i] : -INFINITY;
-      mx = fmaxf(mx, z[kt][i]);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(gr.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(gr.m - m_use);
-  float psum = 0.f;
-  half8_t pf;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(z[kt][i] - m_use);
-      psum += p;
-      pf[4 * kt + i] = (half_t)p;
-    }
-  gr.l = gr.l * alpha + psum;
-  gr.m = m_new;
-#pragma unroll
-  for (int tt = 0; tt < 2 * NB; ++tt) {
-    gr.o[tt] *= alpha;
-    // V^T operand: dim 16tt + l%16, keys 4(l/16)+[0,4) and 16+4(l/16)+[0,4)
-    const half_t* vr = &t.vt[(16 * tt + (lane & 15)) * Tile<NB>::kVStride + 4 * (lane >> 4)];
-    const half4_t a0 = *reinterpret_cast<const half4_t*>(vr);
-    const half4_t a1 = *reinterpret_cast<const half4_t*>(vr + 16);
-    const half8_t vf = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    gr.o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, gr.o[tt], 0, 0, 0);
-  }
+// Element order (0,2,4,6,1,3,5,7): 4-bit codes are unpacked low nibbles first.
+__device__ inline half8_t nibble_order(half8_t q) {
+  return half8_t{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
 }
 
-template <int NB>
-__device__ inline void load_kfrag(half8_t (&kf)[2][NB], float4_t (&kd)[2][NB], const Tile<NB>& t, int lane) {
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      kf[kt][b] = *reinterpret_cast<const half8_t*>(
-          &t.k[(16 * kt + (lane & 15)) * Tile<NB>::kKStride + 32 * b + 8 * (lane >> 4)]);
-      kd[kt][b] = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * (lane >> 4)]);
-    }
-}
+// Max / sum over the two 32-lane halves (lanes l and l^32).  (The gfx950
+// lane-swap builtin was miscompiled here: its second result was dropped.)
+__device__ inline float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+__device__ inline float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
 // ---------------------------------------------------------------------------
-// Decode path: each wave streams raw blocks of its key range into a private
-// LDS stage (coalesced 16-byte loads, the next stage prefetched into
-// registers), and builds its MFMA operands straight from those bytes.
+// Raw stage: the bytes of 32 keys of one KV head, K then V, each as two
+// 16-key runs copied whole (a run never crosses a page: page_size % 16 == 0).
+// Decode waves build MFMA operands from it directly; chunk tiles dequantize it.
 // ---------------------------------------------------------------------------
 
 template <int NB, int KF, int VF>
@@ -428,6 +257,17 @@ struct DecLayout {
   static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
   static_assert(kKBytes % 16 == 0 && kVBytes % 16 == 0 && kWaveBytes % 16 == 0, "alignment");
 };
+
+// Address of 16-byte chunk ch of the stage whose runs start at k0/k1 (K) and
+// v0/v1 (V); chunks past the end re-read the last one.
+template <int NB, int KF, int VF>
+__device__ inline const uint8_t* stage_chunk(int ch, const uint8_t* k0, const uint8_t* k1, const uint8_t* v0,
+                                             const uint8_t* v1) {
+  using L = DecLayout<NB, KF, VF>;
+  if (ch < L::kChunksK) return ch < L::kRecK ? k0 + 16 * ch : k1 + 16 * (ch - L::kRecK);
+  const int cv = min(ch - L::kChunksK, L::kChunksV - 1);
+  return cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
+}
 
 __device__ inline uint32_t lds_u32(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
@@ -626,6 +466,181 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunk path: each 32-key step is dequantized once into a shared LDS tile;
+// every wave serves one query head and 32 rows with 32x32x16 MFMAs.
+// ---------------------------------------------------------------------------
+
+template <int NB>
+struct ChunkTile {
+  static constexpr int kD = 32 * NB;
+  static constexpr int kKStride = kD + 8;         // halves per K row (16-byte rows, skewed banks)
+  static constexpr int kVStride = kStepKeys + 4;  // halves per V^T row (72-byte rows)
+  half_t k[kStepKeys * kKStride];                 // K codes [key][dim], exact integers
+  float kd[NB * kStepKeys];                       // K scale * sm_scale*log2(e), [block][key]
+  half_t vt[kD * kVStride];                       // fp16(V code * V scale), [dim][key]
+};
+
+template <int NB, int KF, int VF>
+struct ChunkLayout {
+  using L = DecLayout<NB, KF, VF>;
+  static constexpr int kTileOff = ((L::kChunks * 16 + 16) + 15) / 16 * 16;  // raw stage first
+  static constexpr int kBytes = kTileOff + 2 * (int)sizeof(ChunkTile<NB>);
+  static constexpr int kLoads = (L::kChunks + 4 * 64 - 1) / (4 * 64);     // per thread, >= 4 waves
+};
+
+// Dequantizes the raw stage into tile t: K as exact integer codes plus fp32
+// scales, V as fp16(code * scale) transposed.  Keys at or past kend become 0.
+template <int NB, int KF, int VF>
+__device__ inline void chunk_dequant(ChunkTile<NB>& t, const uint8_t* raw, int kbase, int kend, int tid, int nthr,
+                                     float zc) {
+  using L = DecLayout<NB, KF, VF>;
+  using T = ChunkTile<NB>;
+  for (int u = tid; u < kStepKeys * NB * 4; u += nthr) {
+    const int kk = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
+    const bool ok = kbase + kk < kend;
+    const int off = L::kKOff + kk * L::kRecK + b * L::kBK;
+    half8_t c = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok) {
+      if constexpr (KF == MAB_KV_Q8) c = lds_codes8_q8(raw, off + 2 + 8 * j);
+      else c = lds_codes8_q4(raw, off + 2 + 4 * j);  // element order (0,2,4,6,1,3,5,7)
+    }
+    *reinterpret_cast<half8_t*>(&t.k[kk * T::kKStride + 32 * b + 8 * j]) = c;
+    if (j == 0)
+      t.kd[b * kStepKeys + kk] =
+          ok ? (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(raw + off)) * zc : 0.f;
+  }
+  for (int u = tid; u < (kStepKeys / 2) * NB * 4; u += nthr) {
+    const int kp = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
+    float vv[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 2 * kp + h;
+      const int off = L::kVOff + kk * L::kRecV + b * L::kBV;
+      if (kbase + kk < kend) {
+        const float d = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(raw + off));
+        half8_t c;
+        if constexpr (VF == MAB_KV_Q8) c = lds_codes8_q8(raw, off + 2 + 8 * j);
+        else c = lds_codes8_q4(raw, off + 2 + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[h][e] = (float)c[e] * d;  // exact in fp32
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[h][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dv = VF == MAB_KV_Q8 ? e : (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+      *reinterpret_cast<half2_t*>(&t.vt[(32 * b + 8 * j + dv) * T::kVStride + 2 * kp]) =
+          half2_t{(half_t)vv[0][e], (half_t)vv[1][e]};
+    }
+  }
+}
+
+// One wave's chunk state: 32 slots = 32 rows of one query head.  Lane l serves
+// slot l%32; the two 32-lane halves hold different keys of S^T and different
+// dims of O^T (32x32 MFMA output layout: element e is row 8(e/4)+4(l/32)+e%4).
+template <int NB>
+struct ChunkWave {
+  half8_t qf[NB][2];   // Q^T operand: slot l%32, dims 32b + 16c + 8(l/32) + [0,8)
+  float16_t o[NB];     // O^T per 32-dim tile
+  float m, l;          // running (possibly stale) max in log2 units; lane-partial sum
+  int limit;           // last visible key of the slot (INT_MAX for padding rows)
+};
+
+template <int NB, int KF>
+__device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* qrow, int limit, int lane) {
+  const int q = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      half8_t v = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      if (qrow) v = *reinterpret_cast<const half8_t*>(qrow + 32 * b + 16 * c + 8 * q);
+      cw.qf[b][c] = KF == MAB_KV_Q4 ? nibble_order(v) : v;
+    }
+#pragma unroll
+  for (int t = 0; t < NB; ++t) cw.o[t] = float16_t{};
+  cw.m = -INFINITY;
+  cw.l = 0.f;
+  cw.limit = qrow ? limit : 0x7fffffff;
+}
+
+template <int NB>
+__device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int kbase, int kend, bool masked,
+                                  int lane) {
+  using T = ChunkTile<NB>;
+  const int q = lane >> 5, n = lane & 31;
+  float16_t s = float16_t{};
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float16_t pb = float16_t{};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const half8_t a = *reinterpret_cast<const half8_t*>(&t.k[n * T::kKStride + 32 * b + 16 * c + 8 * q]);
+      pb = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, cw.qf[b][c], pb, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4_t kd = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 8 * i + 4 * q]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[4 * i + j] += kd[j] * pb[4 * i + j];
+    }
+  }
+  if (masked) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kbase + 8 * (e >> 2) + 4 * q + (e & 3);
+      if (!(key <= cw.limit && key < kend)) s[e] = -INFINITY;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+  mx = max_halves(mx);
+  const float m_new = fmaxf(cw.m, mx);
+  const bool grow = m_new > cw.m + kRescaleSlack;  // also true for the first visible key
+  if (__any(grow)) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f(cw.m - m_new) : 1.f;
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) cw.o[tt] *= alpha;
+    cw.l *= alpha;
+    if (grow) cw.m = m_new;
+  }
+  const float m_use = cw.m == -INFINITY ? 0.f : cw.m;
+  float p[16];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);  // <= 2^8 (stale max), masked keys 0
+    psum += p[e];
+  }
+  cw.l += psum;
+  half8_t pf[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pf[0][e] = (half_t)p[e];
+    pf[1][e] = (half_t)p[8 + e];
+  }
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      // V^T operand: dim 32tt + n; keys 16kh + 4q + [0,4) and 16kh + 8 + 4q + [0,4)
+      const half_t* vr = &t.vt[(32 * tt + n) * T::kVStride + 16 * kh + 4 * q];
+      const half4_t a0 = *reinterpret_cast<const half4_t*>(vr);
+      const half4_t a1 = *reinterpret_cast<const half4_t*>(vr + 8);
+      const half8_t vf = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      cw.o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kh], cw.o[tt], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Work items
+// ---------------------------------------------------------------------------
+
 struct AttnArgs {
   const half_t* q;
   const uint8_t* k_pool;
@@ -645,19 +660,22 @@ struct AttnArgs {
   float c;  // sm_scale * log2(e)
 };
 
-// Locates work item `item` by scanning the per-sequence item counts (chunk
-// sequences first, then decode sequences, each in sequence order).
 struct Found {
   int s, local, item_base;
 };
 
+// Locates work item `item` by scanning the per-sequence item counts (chunk
+// sequences first, then decode sequences, each in sequence order).  Each
+// thread scans a contiguous range of sequences; ranges are combined by a
+// work-group exclusive scan.  sh needs 2*kMaxWaves + 3 ints.
 __device__ inline bool locate_item(const AttnArgs& a, int item, Found& f, int* sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = ceil_div(a.num_seqs, kThreads);
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+  const int G = a.hq / a.hkv;
+  const int per = ceil_div(a.num_seqs, nthr);
   const int s0 = min(a.num_seqs, tid * per), s1 = min(a.num_seqs, s0 + per);
   int c = 0, d = 0;
   for (int s = s0; s < s1; ++s) {
-    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv);
+    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv, G);
     if (p.is_chunk) c += p.items; else d += p.items;
   }
   int ci = c, di = d;  // inclusive wave scan
@@ -666,24 +684,28 @@ __device__ inline bool locate_item(const AttnArgs& a, int item, Found& f, int* s
     const int tc = __shfl_up(ci, off), td = __shfl_up(di, off);
     if (lane >= off) { ci += tc; di += td; }
   }
-  if (lane == 63) { sh[wave] = ci; sh[4 + wave] = di; }
-  if (tid == 0) sh[8] = -1;
+  if (lane == 63) { sh[wave] = ci; sh[kMaxWaves + wave] = di; }
+  if (tid == 0) sh[2 * kMaxWaves] = -1;
   __syncthreads();
   int cb = ci - c, db = di - d, ctot = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) { cb += sh[w]; db += sh[4 + w]; }
+  for (int w = 0; w < nwaves; ++w) {
+    if (w < wave) { cb += sh[w]; db += sh[kMaxWaves + w]; }
     ctot += sh[w];
   }
   for (int s = s0; s < s1; ++s) {
-    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv);
+    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv, G);
     const int base = p.is_chunk ? cb : ctot + db;
-    if (item >= base && item < base + p.items) { sh[8] = s; sh[9] = item - base; sh[10] = base; }
+    if (item >= base && item < base + p.items) {
+      sh[2 * kMaxWaves] = s;
+      sh[2 * kMaxWaves + 1] = item - base;
+      sh[2 * kMaxWaves + 2] = base;
+    }
     if (p.is_chunk) cb += p.items; else db += p.items;
   }
   __syncthreads();
-  f.s = sh[8];
-  f.local = sh[9];
-  f.item_base = sh[10];
+  f.s = sh[2 * kMaxWaves];
+  f.local = sh[2 * kMaxWaves + 1];
+  f.item_base = sh[2 * kMaxWaves + 2];
   __syncthreads();
   return f.s >= 0 && ctot == a.n_chunk_items;
 }
@@ -693,34 +715,191 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
   group_init(gr, qrow, limit, lane);
   if constexpr (KF == MAB_KV_Q4) {  // match the (0,2,4,6,1,3,5,7) order of 4-bit K codes
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const half8_t q = gr.q[b];
-      gr.q[b] = half8_t{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
+    for (int b = 0; b < NB; ++b) gr.q[b] = nibble_order(gr.q[b]);
+  }
+}
+
+// Decode split (row r0, KV head g, keys [kb, ke)): kDecodeWaves waves stream
+// consecutive ranges of 32-key stages (any further waves of a mixed
+// work-group sit this item out, so the arithmetic is the same in both
+// kernels), then merge their softmax states in LDS in wave order.  A row's
+// only split writes the output, others a partial.
+template <int NB, int KF, int VF>
+__device__ inline void decode_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int ctx, int g,
+                                   int kb, int ke, int split_len, bool single, int64_t pbase) {
+  using L = DecLayout<NB, KF, VF>;
+  constexpr int D = 32 * NB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int nw = kDecodeWaves;
+  const int G = a.hq / a.hkv;
+  uint8_t* wbuf = smem + min(wave, nw - 1) * L::kWaveBytes;
+  const int n = lane & 15;
+  Group<NB> gr;
+  dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
+  const int per_wave = ceil_div(split_len / kStepKeys, nw) * kStepKeys;
+  const int kw0 = kb + wave * per_wave;
+  const int kw1 = wave < nw ? min(ke, kw0 + per_wave) : kw0;
+  const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
+  // page ids of the wave's 16-key runs (at most 64), one per lane
+  const int nruns = ceil_div(max(kw1 - kw0, 0), 16);
+  const int my_page = lane < nruns ? ic.bt_row[(kw0 + 16 * lane) / a.page_size] : 0;
+  DecWave<NB, KF, VF> dw;
+  if (nst > 0)
+    dw.load(ic, kw0, kw1, __builtin_amdgcn_readlane(my_page, 0), __builtin_amdgcn_readlane(my_page, 1), lane);
+  for (int st = 0; st < nst; ++st) {
+    const int kbase = kw0 + st * kStepKeys;
+    dw.store(wbuf, lane);
+    asm volatile("" ::: "memory");
+    dec_scales<NB, KF, VF>(wbuf, lane, a.c);
+    if (st + 1 < nst)
+      dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, 2 * st + 2),
+              __builtin_amdgcn_readlane(my_page, 2 * st + 3), lane);
+    asm volatile("" ::: "memory");
+    dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, lane);
+    asm volatile("" ::: "memory");
+  }
+  float lsum = gr.l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // every wave is done with its stage buffer
+  float* mo = reinterpret_cast<float*>(smem);  // [wave][16][D]
+  float* mm = mo + nw * 16 * D;                // [wave][16]
+  float* ml = mm + nw * 16;                    // [wave][16]
+  if (wave < nw) {
+#pragma unroll
+    for (int tt = 0; tt < 2 * NB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo[(wave * 16 + n) * D + 16 * tt + 4 * (lane >> 4) + i] = gr.o[tt][i];
+    if (lane < 16) { mm[wave * 16 + n] = gr.m; ml[wave * 16 + n] = lsum; }
+  }
+  __syncthreads();
+  for (int u = tid; u < G * D; u += blockDim.x) {
+    const int hl = u / D, dd = u % D;
+    float M = -INFINITY;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, mm[w * 16 + hl]);
+    float Ls = 0.f, O = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float sc = __builtin_amdgcn_exp2f(mm[w * 16 + hl] - M);
+      Ls += ml[w * 16 + hl] * sc;
+      O += mo[(w * 16 + hl) * D + dd] * sc;
+    }
+    const int h = g * G + hl;
+    if (single) {
+      a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / Ls;
+    } else {
+      const int64_t pi = pbase + hl;
+      if (pi < a.n_partials) {
+        a.o_part[pi * D + dd] = O;
+        if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
+      }
     }
   }
 }
 
+// Chunk tile (rows qt*R .. qt*R+R-1 of sequence s, KV head g, keys [kb, ke)).
 template <int NB, int KF, int VF>
-constexpr int attn_smem_bytes(bool has_chunk) {
-  constexpr int dec = kWaves * DecLayout<NB, KF, VF>::kWaveBytes;
-  constexpr int merge = (kWaves * 16 * 32 * NB + 2 * kWaves * 16) * 4;
-  constexpr int base = dec > merge ? dec : merge;
-  return has_chunk && (int)sizeof(Tile<NB>) > base ? (int)sizeof(Tile<NB>) : base;
+__device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
+                                  int g, int qt, int kb, int ke, bool single, int64_t pbase) {
+  using L = DecLayout<NB, KF, VF>;
+  using CL = ChunkLayout<NB, KF, VF>;
+  constexpr int D = 32 * NB;
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.hq / a.hkv, R = chunk_rows(G);
+  const int hl = wave % G, rg = wave / G;
+  uint8_t* raw = smem;
+  ChunkTile<NB>* tiles = reinterpret_cast<ChunkTile<NB>*>(smem + CL::kTileOff);
+
+  const int row_in_tile = 32 * rg + (lane & 31);
+  const int i = qt * R + row_in_tile;
+  ChunkWave<NB> cw;
+  chunk_wave_init<NB, KF>(cw, i < q_len ? a.q + ((int64_t)(r0 + i) * a.hq + g * G + hl) * D : nullptr, prefix + i,
+                          lane);
+  const int first_row = prefix + qt * R + 32 * rg;  // smallest limit among the wave's rows
+  const bool wave_live = qt * R + 32 * rg < q_len;
+
+  const int nsteps = ceil_div(ke - kb, kStepKeys);
+  const int ps = a.page_size;
+  auto run_addr = [&](int key, int page, const uint8_t* pool, int rec) {
+    return pool + (((int64_t)page * ic.hkv + g) * ps + key % ps) * rec;
+  };
+  u32x4_t r[CL::kLoads];
+  // raw loads of step st (keys at or past ke re-read run 0, masked later)
+  auto load = [&](int st, int page0, int page1) {
+    const int kbase = kb + st * kStepKeys, key1 = kbase + 16;
+    const bool ok1 = key1 < ke;
+    const uint8_t* k0 = run_addr(kbase, page0, ic.k_pool, L::kRecK);
+    const uint8_t* v0 = run_addr(kbase, page0, ic.v_pool, L::kRecV);
+    const uint8_t* k1 = ok1 ? run_addr(key1, page1, ic.k_pool, L::kRecK) : k0;
+    const uint8_t* v1 = ok1 ? run_addr(key1, page1, ic.v_pool, L::kRecV) : v0;
+#pragma unroll
+    for (int u = 0; u < CL::kLoads; ++u)
+      r[u] = *reinterpret_cast<const u32x4_t*>(stage_chunk<NB, KF, VF>(tid + nthr * u, k0, k1, v0, v1));
+  };
+  auto page_of = [&](int key) { return key < ke ? ic.bt_row[key / ps] : 0; };
+  int pg0 = page_of(kb), pg1 = page_of(kb + 16);
+  load(0, pg0, pg1);
+  pg0 = page_of(kb + kStepKeys);
+  pg1 = page_of(kb + kStepKeys + 16);
+  for (int st = 0; st < nsteps; ++st) {
+    const int kbase = kb + st * kStepKeys;
+#pragma unroll
+    for (int u = 0; u < CL::kLoads; ++u) {
+      const int ch = tid + nthr * u;
+      if (ch < L::kChunks) *reinterpret_cast<u32x4_t*>(raw + 16 * ch) = r[u];
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) {
+      load(st + 1, pg0, pg1);
+      pg0 = page_of(kbase + 2 * kStepKeys);
+      pg1 = page_of(kbase + 2 * kStepKeys + 16);
+    }
+    ChunkTile<NB>& t = tiles[st & 1];
+    chunk_dequant<NB, KF, VF>(t, raw, kbase, ke, tid, nthr, a.c);
+    __syncthreads();
+    if (wave_live) {
+      const bool masked = kbase + kStepKeys - 1 > first_row || kbase + kStepKeys > ke;
+      chunk_step<NB>(cw, t, kbase, ke, masked, lane);
+    }
+  }
+  const float ltot = sum_halves(cw.l);
+  if (i >= q_len) return;
+  const int h = g * G + hl;
+  const int q = lane >> 5;
+  if (single) {
+    const float inv = 1.f / ltot;
+    float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * q;
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
+            float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]} * inv;
+  } else {
+    const int64_t pi = pbase + (int64_t)hl * R + row_in_tile;
+    if (pi < a.n_partials) {
+      float* dst = a.o_part + pi * D + 4 * q;
+#pragma unroll
+      for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
+              float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]};
+      if (q == 0) a.ml_part[pi] = make_float2(cw.m, ltot);
+    }
+  }
 }
 
 template <int NB, int KF, int VF, bool HAS_CHUNK>
 __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem, int* sh) {
-  constexpr int D = 32 * NB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int item = blockIdx.x;
-
   Found f;
   if (!locate_item(a, item, f, sh)) return;
   const int s = f.s;
   const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
   const int ctx = prefix + q_len;
-  const SeqPlan p = plan_seq(q_len, prefix, a.hkv);
-  const int G = a.hq / a.hkv;
+  const int G = a.hq / a.hkv, R = chunk_rows(G);
+  const SeqPlan p = plan_seq(q_len, prefix, a.hkv, G);
 
   int qt, g, j;
   if (p.is_chunk) {
@@ -735,20 +914,16 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem, int* sh)
   }
   if (tid == 0 && f.local == 0) a.seq_base[s] = f.item_base;
   if (g == 0 && j == 0) {
-    const int rows = p.is_chunk ? kChunkRows : 1;
-    for (int r = tid; r < rows; r += kThreads) {
-      const int i = qt * kChunkRows + r;
+    const int rows = p.is_chunk ? R : 1;
+    for (int r = tid; r < rows; r += blockDim.x) {
+      const int i = qt * R + r;
       if (i < q_len) a.row_seq[r0 + i] = s;
     }
   }
-
   const int kb = j * p.split_len;
   int ke = min(ctx, kb + p.split_len);
-  if (p.is_chunk) {
-    const int last_row = min(q_len, (qt + 1) * kChunkRows) - 1;
-    ke = min(ke, prefix + last_row + 1);
-    if (kb >= ke) return;  // no row of this tile sees this split
-  }
+  if (p.is_chunk) ke = min(ke, prefix + min(q_len, (qt + 1) * R));  // past the tile's last row
+  if (kb >= ke) return;  // no row of this tile sees this split
   const int64_t pbase = partial_base(item, a.n_chunk_items, G);
   const bool single = p.n_split == 1;
 
@@ -761,147 +936,42 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem, int* sh)
   ic.page_size = a.page_size;
 
   if (!p.is_chunk) {
-    // Decode split: wave w streams keys [kb + w*len/4, kb + (w+1)*len/4) in
-    // 32-key stages; the waves then merge their softmax states in wave order.
-    using L = DecLayout<NB, KF, VF>;
-    uint8_t* wbuf = smem + wave * L::kWaveBytes;
-    const int n = lane & 15;
-    Group<NB> gr;
-    dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
-    const int per_wave = p.split_len / kWaves;
-    const int kw0 = kb + wave * per_wave;
-    const int kw1 = min(ke, kw0 + per_wave);
-    const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
-    // page ids of the wave's 16-key runs (at most 64), one per lane
-    const int nruns = ceil_div(max(kw1 - kw0, 0), 16);
-    const int my_page = lane < nruns ? ic.bt_row[(kw0 + 16 * lane) / a.page_size] : 0;
-    DecWave<NB, KF, VF> dw;
-    if (nst > 0)
-      dw.load(ic, kw0, kw1, __builtin_amdgcn_readlane(my_page, 0), __builtin_amdgcn_readlane(my_page, 1), lane);
-    for (int st = 0; st < nst; ++st) {
-      const int kbase = kw0 + st * kStepKeys;
-      dw.store(wbuf, lane);
-      asm volatile("" ::: "memory");
-      dec_scales<NB, KF, VF>(wbuf, lane, a.c);
-      if (st + 1 < nst)
-        dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, 2 * st + 2),
-                __builtin_amdgcn_readlane(my_page, 2 * st + 3), lane);
-      asm volatile("" ::: "memory");
-      dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, lane);
-      asm volatile("" ::: "memory");
-    }
-    float lsum = gr.l;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    __syncthreads();  // every wave is done with its stage buffer
-    float* mo = reinterpret_cast<float*>(smem);  // [wave][16][D]
-    float* mm = mo + kWaves * 16 * D;            // [wave][16]
-    float* ml = mm + kWaves * 16;                // [wave][16]
-#pragma unroll
-    for (int tt = 0; tt < 2 * NB; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mo[(wave * 16 + n) * D + 16 * tt + 4 * (lane >> 4) + i] = gr.o[tt][i];
-    if (lane < 16) { mm[wave * 16 + n] = gr.m; ml[wave * 16 + n] = lsum; }
-    __syncthreads();
-    for (int u = tid; u < G * D; u += kThreads) {
-      const int hl = u / D, dd = u % D;
-      float M = -INFINITY;
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + hl]);
-      float Ls = 0.f, O = 0.f;
-      for (int w = 0; w < kWaves; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(mm[w * 16 + hl] - M);
-        Ls += ml[w * 16 + hl] * sc;
-        O += mo[(w * 16 + hl) * D + dd] * sc;
-      }
-      const int h = g * G + hl;
-      if (single) {
-        a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / Ls;
-      } else {
-        const int64_t pi = pbase + hl;
-        if (pi < a.n_partials) {
-          a.o_part[pi * D + dd] = O;
-          if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
-        }
-      }
-    }
-    return;
+    decode_item<NB, KF, VF>(a, smem, ic, r0, ctx, g, kb, ke, p.split_len, single, pbase);
+  } else if constexpr (HAS_CHUNK) {
+    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, qt, kb, ke, single, pbase);
   }
-
-  if constexpr (!HAS_CHUNK) {
-    return;
-  } else {
-  Tile<NB>* tiles = reinterpret_cast<Tile<NB>*>(smem);
-  const int nsteps = ceil_div(ke - kb, kStepKeys);
-  // Chunk tile: 32 rows x G heads = 2G groups of 16 slots, dealt round-robin to
-  // the four waves; all waves share one tile per step.
-  Group<NB> grs[kMaxGroupsPerWave];
-  const int ngroups = 2 * G;
-#pragma unroll
-  for (int k = 0; k < kMaxGroupsPerWave; ++k) {
-    const int gi = wave + kWaves * k;
-    const int hl = gi >> 1, half_rows = gi & 1;
-    const int i = qt * kChunkRows + 16 * half_rows + (lane & 15);
-    const half_t* qrow = (gi < ngroups && i < q_len) ? a.q + ((int64_t)(r0 + i) * a.hq + g * G + hl) * D
-                                                     : nullptr;
-    group_init(grs[k], qrow, prefix + i, lane);
-  }
-  for (int st = 0; st < nsteps; ++st) {
-    const int kbase = kb + st * kStepKeys;
-    produce_tile<NB, KF, VF>(tiles[0], ic, kbase, ke, tid, kThreads, a.c);
-    __syncthreads();
-    half8_t kf[2][NB];
-    float4_t kd[2][NB];
-    load_kfrag(kf, kd, tiles[0], lane);
-#pragma unroll
-    for (int k = 0; k < kMaxGroupsPerWave; ++k)
-      if (wave + kWaves * k < ngroups) group_step(grs[k], tiles[0], kf, kd, kbase, ke, lane);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxGroupsPerWave; ++k) {
-    const int gi = wave + kWaves * k;
-    if (gi >= ngroups) continue;
-    const int hl = gi >> 1, half_rows = gi & 1;
-    const int r = 16 * half_rows + (lane & 15);
-    const int i = qt * kChunkRows + r;
-    float lsum = grs[k].l;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (i >= q_len) continue;
-    const int h = g * G + hl;
-    if (single) {
-      const float inv = 1.f / lsum;
-      float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * (lane >> 4);
-#pragma unroll
-      for (int tt = 0; tt < 2 * NB; ++tt) *reinterpret_cast<float4_t*>(dst + 16 * tt) = grs[k].o[tt] * inv;
-    } else {
-      const int64_t pi = pbase + (int64_t)hl * kChunkRows + r;
-      if (pi < a.n_partials) {
-        float* dst = a.o_part + pi * D + 4 * (lane >> 4);
-#pragma unroll
-        for (int tt = 0; tt < 2 * NB; ++tt) *reinterpret_cast<float4_t*>(dst + 16 * tt) = grs[k].o[tt];
-        if (lane < 16) a.ml_part[pi] = make_float2(grs[k].m, lsum);
-      }
-    }
-  }
-  }  // HAS_CHUNK
 }
 
-// Batches with a chunk: heavy chunk tiles and decode splits in one launch.
 template <int NB, int KF, int VF>
-__global__ void __launch_bounds__(kThreads)
+constexpr int decode_smem_bytes(int waves) {
+  const int stages = waves * DecLayout<NB, KF, VF>::kWaveBytes;
+  const int merge = (waves * 16 * 32 * NB + 2 * waves * 16) * 4;
+  return stages > merge ? stages : merge;
+}
+
+template <int NB, int KF, int VF>
+constexpr int mixed_smem_bytes() {
+  const int dec = decode_smem_bytes<NB, KF, VF>(kDecodeWaves);
+  const int chunk = ChunkLayout<NB, KF, VF>::kBytes;
+  return dec > chunk ? dec : chunk;
+}
+
+// Batches with a chunk: heavy chunk tiles and decode splits in one launch of
+// G*ceil(4/G) waves per work-group.
+template <int NB, int KF, int VF>
+__global__ void __launch_bounds__(64 * kMaxWaves)
 mixed_attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(true)];
-  __shared__ int sh[16];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
+  __shared__ int sh[2 * kMaxWaves + 4];
   attention_body<NB, KF, VF, true>(a, smem, sh);
 }
 
-// Decode-only batches: the same decode splits, compiled for at least three waves per SIMD.
+// Decode-only batches: kDecodeWaves waves per work-group, at least three per SIMD.
 template <int NB, int KF, int VF>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 8)))
 decode_attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<NB, KF, VF>(false)];
-  __shared__ int sh[16];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF>(kDecodeWaves)];
+  __shared__ int sh[2 * kMaxWaves + 4];
   attention_body<NB, KF, VF, false>(a, smem, sh);
 }
 
@@ -918,19 +988,19 @@ combine_kernel(AttnArgs a, int head_dim) {
   const int row = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
   const int s = a.row_seq[row];
   if (s < 0 || s >= a.num_seqs) return;
+  const int G = a.hq / a.hkv, R = chunk_rows(G);
   const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
-  const SeqPlan p = plan_seq(q_len, prefix, a.hkv);
+  const SeqPlan p = plan_seq(q_len, prefix, a.hkv, G);
   if (p.n_split == 1) return;
   const int item_base = a.seq_base[s];
-  const int G = a.hq / a.hkv;
   const int i = row - r0;
   if (i < 0 || i >= q_len || item_base < 0 || item_base >= a.n_items) return;
   const int nj = (prefix + i) / p.split_len + 1;
-  const int qt = i / kChunkRows, rr = i % kChunkRows;
+  const int qt = i / R, rr = i % R;
   const int g = h / G, hl = h % G;
   auto pidx = [&](int jj) -> int64_t {
     const int item = p.is_chunk ? item_base + qt + p.n_qt * (jj + p.n_split * g) : item_base + g * p.n_split + jj;
-    return partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? hl * kChunkRows + rr : hl);
+    return partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? (int64_t)hl * R + rr : hl);
   };
   float M = -INFINITY;
   for (int jj = tid; jj < nj; jj += blockDim.x) {
@@ -1003,14 +1073,14 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     if (q_len < 1 || prefix < 0) return MAB_ERR_SHAPE;
     const int64_t ctx = prefix + q_len;
     if (ctx > (int64_t)B->max_pages_per_seq * L->page_size || ctx > (int64_t)1 << 30) return MAB_ERR_SHAPE;
-    const SeqPlan p = plan_seq((int)q_len, (int)prefix, L->num_kv_heads);
+    const SeqPlan p = plan_seq((int)q_len, (int)prefix, L->num_kv_heads, G);
     if (p.is_chunk) chunk += p.items; else dec += p.items;
   }
   if (chunk + dec > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
   if (hp) {
     hp->n_chunk_items = chunk;
     hp->n_items = chunk + dec;
-    hp->n_partials = chunk * G * kChunkRows + dec * G;
+    hp->n_partials = chunk * G * chunk_rows(G) + dec * G;
   }
   return MAB_OK;
 }
@@ -1031,9 +1101,10 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 template <int NB, int KF, int VF>
 void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * mixed_waves(a.hq / a.hkv)), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
 }
 
 template <int NB>
