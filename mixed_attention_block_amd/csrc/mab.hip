@@ -11,13 +11,15 @@
 //   mixed_attention_kernel  -- one launch over a flat list of work items: chunk
 //                              tiles first (heavy), then decode splits.
 //   decode_attention_kernel -- the same decode splits for batches without a chunk.
-//   combine_kernel          -- log-sum-exp merge of split-K partials in fixed order.
 // Decode splits stream raw blocks per wave and build 16x16x32 MFMA operands from
 // the bytes; chunk tiles dequantize each 32-key step once into a shared LDS tile
 // and run 32x32x16 MFMAs.  Keys always enter the MFMA as exact integer codes with
 // their block scale applied in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "mab.h"
 
@@ -34,12 +36,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte 
 constexpr int kDecodeWaves = 4;     // waves that stream a decode split (in either kernel)
 constexpr int kMaxWaves = 8;        // waves of a mixed work-group (G * ceil(4/G) <= 8)
 constexpr int kStepKeys = 32;       // keys per stage / tile
-constexpr int kDecodeSplit = 2048;  // shortest decode split (multiple of kMaxWaves*kStepKeys)
-constexpr int kMaxDecodeSplit = 4096;  // longest decode split: at most 64 16-key runs per wave
-constexpr int kMaxDecodeSplits = 128;
-constexpr int kChunkSplit = 65536;  // keys per chunk split (multiple of kStepKeys)
+constexpr int kChunkSplit = 1 << 30;  // keys per chunk split (no split: a tile sees all its keys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr int kMaxSeqs = 4096;
+constexpr int kDecWGsPerCU = 3;     // decode work-groups resident per compute unit
+constexpr int kMinWGStages = 16;    // a decode work-group streams at least this many stages
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
 
@@ -48,6 +49,7 @@ template <> struct Fmt<MAB_KV_Q8> { static constexpr int kBytes = 34; static con
 template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static constexpr int kQmax = 7; };
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Waves of a mixed work-group and rows of a chunk tile: every wave of a chunk
 // tile serves one query head of the group and 32 rows, so a tile has
@@ -55,52 +57,40 @@ __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; 
 __host__ __device__ inline int mixed_waves(int group) { return group * ceil_div(4, group); }
 __host__ __device__ inline int chunk_rows(int group) { return 32 * ceil_div(4, group); }
 
-// Work-item bookkeeping shared by host and device.  A sequence with more than
-// one row is a chunk: ceil(q_len/rows) row tiles x Hkv x ceil(ctx/kChunkSplit)
-// key splits.  A one-row sequence is a decode row: Hkv x ceil(ctx/split_len).
-struct SeqPlan {
-  int is_chunk, n_qt, n_split, split_len, items;
-};
-
-// Keys per decode split: kDecodeSplit, doubled (up to kMaxDecodeSplit) until
-// the row has at most kMaxDecodeSplits splits.  It depends only on the row's
-// own context, so a row's arithmetic is the same whatever shares the batch.
-__host__ __device__ inline int decode_split_len(int ctx) {
-  int len = kDecodeSplit;
-  while ((int64_t)len * kMaxDecodeSplits < ctx && len < kMaxDecodeSplit) len *= 2;
-  return len;
+// A sequence with more than one row is a chunk: ceil(q_len/rows) row tiles x
+// Hkv work items.  A one-row sequence is a decode row: Hkv segments of
+// ceil(ctx/32) stages each in the decode stream.
+__host__ __device__ inline int chunk_items(int q_len, int hkv, int group) {
+  return ceil_div(q_len, chunk_rows(group)) * hkv;
 }
-
-__host__ __device__ inline SeqPlan plan_seq(int q_len, int prefix, int hkv, int group) {
-  SeqPlan p;
-  const int ctx = prefix + q_len;
-  p.is_chunk = q_len > 1;
-  p.n_qt = p.is_chunk ? ceil_div(q_len, chunk_rows(group)) : 1;
-  p.split_len = p.is_chunk ? kChunkSplit : decode_split_len(ctx);
-  p.n_split = ceil_div(ctx, p.split_len);
-  p.items = p.n_qt * hkv * p.n_split;
-  return p;
-}
-
-// Partial-result slots: a chunk item owns G*rows slots, a decode item G slots.
-__host__ __device__ inline int64_t partial_base(int64_t item, int64_t n_chunk_items, int group) {
-  const int64_t cs = (int64_t)group * chunk_rows(group);
-  return item < n_chunk_items ? item * cs : n_chunk_items * cs + (item - n_chunk_items) * group;
-}
+__host__ __device__ inline int dec_stages(int ctx) { return ceil_div(ctx, kStepKeys); }
 
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-struct WsLayout {
-  int64_t o_off, ml_off, row_seq_off, seq_base_off, total;
+// Where a decode segment's results went: its first piece's partial slot, the
+// decode work-group that ran that piece, the number of pieces (1: the output
+// was written directly) and the segment's first output row-head.
+struct DirEntry {
+  int slot, wg, n, rh0;
 };
 
-__host__ __device__ inline WsLayout ws_layout(int64_t n_partials, int num_rows, int num_seqs, int head_dim) {
+// Workspace: decode partials (slot = work-group * pmax + piece; o fp32
+// [slot][G][D], (m, l) fp32 pairs [slot][G]), one directory entry per decode
+// segment, and the launch-order tables for batches too large for the kernel
+// arguments.  Nothing needs initialising: every entry read is written first in
+// the same call.
+struct WsLayout {
+  int64_t o_off, ml_off, dir_off, tab_off, total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int64_t n_slots, int group, int head_dim, int64_t n_dec_segs,
+                                              int64_t tab_ints) {
   WsLayout w;
   w.o_off = 0;
-  w.ml_off = align256(w.o_off + n_partials * head_dim * 4);
-  w.row_seq_off = align256(w.ml_off + n_partials * 8);
-  w.seq_base_off = align256(w.row_seq_off + (int64_t)num_rows * 4);
-  w.total = align256(w.seq_base_off + (int64_t)num_seqs * 4);
+  w.ml_off = align256(w.o_off + n_slots * group * head_dim * 4);
+  w.dir_off = align256(w.ml_off + n_slots * group * 8);
+  w.tab_off = align256(w.dir_off + n_dec_segs * (int64_t)sizeof(DirEntry));
+  w.total = align256(w.tab_off + tab_ints * 4);
   return w;
 }
 
@@ -354,7 +344,7 @@ struct DecWave {
             : ch < L::kChunksK ? k1 + 16 * (ch - L::kRecK)
             : cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
       }
-      r[i] = *reinterpret_cast<const u32x4_t*>(src);
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));  // streamed once
     }
   }
 
@@ -367,8 +357,10 @@ struct DecWave {
 
 // Pulls the K and V block scales of the stage in LDS into the compact arrays:
 // K scales as fp32 times c = sm_scale*log2(e), V scales as fp16, both [block][key].
+// Keys at or past kend get scale 0, so their (possibly NaN) bytes never reach
+// a sum: their logits become exactly 0 before masking and their P*scale 0.
 template <int NB, int KF, int VF>
-__device__ inline void dec_scales(uint8_t* w, int lane, float zc) {
+__device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
   using L = DecLayout<NB, KF, VF>;
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
@@ -376,20 +368,24 @@ __device__ inline void dec_scales(uint8_t* w, int lane, float zc) {
     const bool isv = q >= NB / 2;
     const int m = isv ? idx - 32 * NB : idx;
     const int b = m / kStepKeys, key = m % kStepKeys;
+    const bool ok = key < nvalid;
     if (!isv) {
       const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kKOff + key * L::kRecK + b * L::kBK);
-      reinterpret_cast<float*>(w + L::kSKOff)[m] = (float)__builtin_bit_cast(half_t, bits) * zc;
+      reinterpret_cast<float*>(w + L::kSKOff)[m] = ok ? (float)__builtin_bit_cast(half_t, bits) * zc : 0.f;
     } else {
       const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
-      reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = bits;
+      reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = ok ? bits : (uint16_t)0;
     }
   }
 }
 
 // One 32-key stage of a decode wave: S^T = K Q^T on integer codes per block,
-// fp32 block scales, online softmax, then O^T += V^T (P * V scale).
+// fp32 block scales, online softmax with a stale max (rescaled only when the
+// running max grows by more than 2^kRescaleSlack), then O^T += V^T (P * V
+// scale) with P rounded to fp16 once and multiplied by the fp16 V scale of
+// each block.  `tail`: the stage holds keys at or past kend (masked).
 template <int NB, int KF, int VF>
-__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, int lane) {
+__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, int lane) {
   using L = DecLayout<NB, KF, VF>;
   const int j = lane >> 4, n = lane & 15;
   float4_t s[2];
@@ -408,48 +404,45 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
       s[kt] += kd * pb;
     }
   }
-  float z[8];
-  float mx = -INFINITY;
+  if (tail) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kbase + 16 * kt + 4 * j + i >= kend) s[kt][i] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool grow = mx > gr.m + kRescaleSlack;  // also true for the first keys (m = -inf)
+  if (__any(grow)) {
+    const float m_new = grow ? mx : gr.m;
+    const float alpha = __builtin_amdgcn_exp2f(gr.m - m_new);  // 0 when m was -inf
+#pragma unroll
+    for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
+    gr.l *= alpha;
+    gr.m = m_new;
+  }
+  float p[8];
+  float psum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = kbase + 16 * kt + 4 * j + i;
-      z[4 * kt + i] = (key < kend && key <= gr.limit) ? s[kt][i] : -INFINITY;
-      mx = fmaxf(mx, z[4 * kt + i]);
+      p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][i] - gr.m);  // <= 2^kRescaleSlack; masked keys 0
+      psum += p[4 * kt + i];
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(gr.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(gr.m - m_use);
-  float p[8];
-  float psum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = __builtin_amdgcn_exp2f(z[e] - m_use);  // masked keys: exactly 0
-    psum += p[e];
-  }
-  gr.l = gr.l * alpha + psum;
-  gr.m = m_new;
-#pragma unroll
-  for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
-  // keys of this lane's P operand: 4j+[0,4) and 16+4j+[0,4); V scales of keys
-  // past kend may be garbage (even NaN), so their P' is forced to 0.
-  bool ok[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ok[e] = kbase + ((e < 4) ? 4 * j + e : 12 + 4 * j + e) < kend;
+  gr.l += psum;
+  // P as fp16 in the key order of the PV operand: 4j+[0,4) then 16+4j+[0,4)
+  const half8_t ph = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
+                             (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
   const half_t* sv = reinterpret_cast<const half_t*>(w + L::kSVOff);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const half4_t s0 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 4 * j);
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
-    half8_t pf;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pf[e] = ok[e] ? (half_t)(p[e] * (float)s0[e]) : (half_t)0.f;
-      pf[4 + e] = ok[4 + e] ? (half_t)(p[4 + e] * (float)s1[e]) : (half_t)0.f;
-    }
+    const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int dv = 16 * t2 + n;  // value index inside block b
@@ -638,8 +631,48 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 }
 
 // ---------------------------------------------------------------------------
-// Work items
+// Launch plan.  The grid holds the chunk work items first (one work-group per
+// row tile and KV head), then the decode stream: the stages of every decode
+// segment (one decode row and KV head) laid end to end, cut into equal
+// contiguous ranges, one per decode work-group, so every work-group streams
+// the same number of bytes.  A range that holds a whole segment writes its
+// output; pieces of a longer segment write partials that combine_kernel merges
+// in range order.
 // ---------------------------------------------------------------------------
+
+// Launch-order tables of the sequences.  Decode entry e (a one-row sequence):
+// its Hkv segments of dec_stages(ctx) stages each start at dec_unit[e] +
+// g*dec_stages(ctx).  Chunk entry c: work items [ch_item[c], ch_item[c+1]).
+// Small batches carry them in the kernel arguments; larger ones have
+// plan_kernel write them to the workspace.
+constexpr int kArgDec = 96;
+constexpr int kArgChunk = 16;
+
+struct ArgTabs {
+  int dec_unit[kArgDec + 1], dec_seq[kArgDec], dec_r0[kArgDec], dec_ctx[kArgDec];
+  int ch_item[kArgChunk + 1], ch_seq[kArgChunk], ch_r0[kArgChunk], ch_qlen[kArgChunk], ch_prefix[kArgChunk];
+};
+
+// Offsets (in ints) of the tables in the workspace.
+struct WsTabs {
+  int dec_unit, dec_seq, dec_r0, dec_ctx, ch_item, ch_seq, ch_r0, ch_qlen, ch_prefix, total;
+};
+
+__host__ __device__ inline WsTabs ws_tabs(int n_dec, int n_chunk) {
+  WsTabs t;
+  int o = 0;
+  t.dec_unit = o; o += n_dec + 1;
+  t.dec_seq = o; o += n_dec;
+  t.dec_r0 = o; o += n_dec;
+  t.dec_ctx = o; o += n_dec;
+  t.ch_item = o; o += n_chunk + 1;
+  t.ch_seq = o; o += n_chunk;
+  t.ch_r0 = o; o += n_chunk;
+  t.ch_qlen = o; o += n_chunk;
+  t.ch_prefix = o; o += n_chunk;
+  t.total = o;
+  return t;
+}
 
 struct AttnArgs {
   const half_t* q;
@@ -651,63 +684,53 @@ struct AttnArgs {
   float* out;
   float* o_part;
   float2* ml_part;
-  int32_t* row_seq;
-  int32_t* seq_base;
-  int64_t n_partials;
-  int num_seqs, num_rows, max_pages;
+  DirEntry* dir;
+  int32_t* ws_tab;
+  int num_seqs, max_pages;
   int hq, hkv, page_size;
-  int n_chunk_items, n_items;
-  float c;  // sm_scale * log2(e)
+  int n_dec, n_chunk;       // decode and chunk sequences
+  int n_chunk_items;        // chunk work items (the first entries of the grid)
+  int dec_units;            // stages in the decode stream
+  int dec_range;            // stages per decode work-group (the last may have fewer)
+  int dec_pmax;             // partial slots per decode work-group
+  int tabs_in_ws;           // tables in the workspace (1) or in `tabs` (0)
+  float c;                  // sm_scale * log2(e)
+  ArgTabs tabs;
 };
 
-struct Found {
-  int s, local, item_base;
+struct TabView {
+  const int *dec_unit, *dec_seq, *dec_r0, *dec_ctx;
+  const int *ch_item, *ch_seq, *ch_r0, *ch_qlen, *ch_prefix;
 };
 
-// Locates work item `item` by scanning the per-sequence item counts (chunk
-// sequences first, then decode sequences, each in sequence order).  Each
-// thread scans a contiguous range of sequences; ranges are combined by a
-// work-group exclusive scan.  sh needs 2*kMaxWaves + 3 ints.
-__device__ inline bool locate_item(const AttnArgs& a, int item, Found& f, int* sh) {
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-  const int G = a.hq / a.hkv;
-  const int per = ceil_div(a.num_seqs, nthr);
-  const int s0 = min(a.num_seqs, tid * per), s1 = min(a.num_seqs, s0 + per);
-  int c = 0, d = 0;
-  for (int s = s0; s < s1; ++s) {
-    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv, G);
-    if (p.is_chunk) c += p.items; else d += p.items;
+__device__ inline TabView tab_view(const AttnArgs& a) {
+  TabView v;
+  if (a.tabs_in_ws) {
+    const WsTabs t = ws_tabs(a.n_dec, a.n_chunk);
+    const int* b = a.ws_tab;
+    v.dec_unit = b + t.dec_unit; v.dec_seq = b + t.dec_seq; v.dec_r0 = b + t.dec_r0; v.dec_ctx = b + t.dec_ctx;
+    v.ch_item = b + t.ch_item; v.ch_seq = b + t.ch_seq; v.ch_r0 = b + t.ch_r0; v.ch_qlen = b + t.ch_qlen;
+    v.ch_prefix = b + t.ch_prefix;
+  } else {
+    v.dec_unit = a.tabs.dec_unit; v.dec_seq = a.tabs.dec_seq; v.dec_r0 = a.tabs.dec_r0; v.dec_ctx = a.tabs.dec_ctx;
+    v.ch_item = a.tabs.ch_item; v.ch_seq = a.tabs.ch_seq; v.ch_r0 = a.tabs.ch_r0; v.ch_qlen = a.tabs.ch_qlen;
+    v.ch_prefix = a.tabs.ch_prefix;
   }
-  int ci = c, di = d;  // inclusive wave scan
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int tc = __shfl_up(ci, off), td = __shfl_up(di, off);
-    if (lane >= off) { ci += tc; di += td; }
+  return v;
+}
+
+// Index of the last entry e < n with base[e] <= x (base strictly increasing,
+// base[0] <= x): every lane tests one entry per pass, so the search costs one
+// round trip per 64 entries instead of a chain of dependent loads.
+__device__ inline int wave_find(const int* base, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    const bool le = e < n && base[e] <= x;
+    cnt += __popcll(__ballot(le));
   }
-  if (lane == 63) { sh[wave] = ci; sh[kMaxWaves + wave] = di; }
-  if (tid == 0) sh[2 * kMaxWaves] = -1;
-  __syncthreads();
-  int cb = ci - c, db = di - d, ctot = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    if (w < wave) { cb += sh[w]; db += sh[kMaxWaves + w]; }
-    ctot += sh[w];
-  }
-  for (int s = s0; s < s1; ++s) {
-    const SeqPlan p = plan_seq(a.q_start[s + 1] - a.q_start[s], a.prefix_len[s], a.hkv, G);
-    const int base = p.is_chunk ? cb : ctot + db;
-    if (item >= base && item < base + p.items) {
-      sh[2 * kMaxWaves] = s;
-      sh[2 * kMaxWaves + 1] = item - base;
-      sh[2 * kMaxWaves + 2] = base;
-    }
-    if (p.is_chunk) cb += p.items; else db += p.items;
-  }
-  __syncthreads();
-  f.s = sh[2 * kMaxWaves];
-  f.local = sh[2 * kMaxWaves + 1];
-  f.item_base = sh[2 * kMaxWaves + 2];
-  __syncthreads();
-  return f.s >= 0 && ctot == a.n_chunk_items;
+  return cnt - 1;
 }
 
 template <int NB, int KF>
@@ -719,14 +742,15 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
   }
 }
 
-// Decode split (row r0, KV head g, keys [kb, ke)): kDecodeWaves waves stream
-// consecutive ranges of 32-key stages (any further waves of a mixed
-// work-group sit this item out, so the arithmetic is the same in both
-// kernels), then merge their softmax states in LDS in wave order.  A row's
-// only split writes the output, others a partial.
+// One piece of a decode segment (row r0 of sequence s, KV head g, keys
+// [kb, ke), kb a multiple of 32): the kDecodeWaves waves stream consecutive
+// ranges of 32-key stages, one stage ahead, with loads that bypass the caches'
+// retention (every byte is read once), then merge their softmax states in LDS
+// in wave order.  Any further waves of a mixed work-group sit the piece out.
+// A whole segment writes the output, a piece its partial at `slot`.
 template <int NB, int KF, int VF>
-__device__ inline void decode_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int ctx, int g,
-                                   int kb, int ke, int split_len, bool single, int64_t pbase) {
+__device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int r0, int ctx, int g, int kb,
+                                    int ke, bool whole, int slot) {
   using L = DecLayout<NB, KF, VF>;
   constexpr int D = 32 * NB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -734,15 +758,25 @@ __device__ inline void decode_item(const AttnArgs& a, uint8_t* smem, const ItemC
   const int G = a.hq / a.hkv;
   uint8_t* wbuf = smem + min(wave, nw - 1) * L::kWaveBytes;
   const int n = lane & 15;
-  Group<NB> gr;
-  dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
-  const int per_wave = ceil_div(split_len / kStepKeys, nw) * kStepKeys;
+  ItemCtx ic;
+  ic.k_pool = a.k_pool;
+  ic.v_pool = a.v_pool;
+  ic.bt_row = a.block_table + (int64_t)s * a.max_pages;
+  ic.hkv = a.hkv;
+  ic.g = g;
+  ic.page_size = a.page_size;
+  const int per_wave = ceil_div(ceil_div(ke - kb, kStepKeys), nw) * kStepKeys;
   const int kw0 = kb + wave * per_wave;
   const int kw1 = wave < nw ? min(ke, kw0 + per_wave) : kw0;
   const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
-  // page ids of the wave's 16-key runs (at most 64), one per lane
-  const int nruns = ceil_div(max(kw1 - kw0, 0), 16);
-  const int my_page = lane < nruns ? ic.bt_row[(kw0 + 16 * lane) / a.page_size] : 0;
+  // page ids of the wave's 16-key runs, 64 at a time (one per lane)
+  auto page_window = [&](int win) {
+    const int key = kw0 + 16 * (64 * win + lane);
+    return key < kw1 ? ic.bt_row[key / a.page_size] : 0;
+  };
+  int my_page = page_window(0);
+  Group<NB> gr;
+  dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
   DecWave<NB, KF, VF> dw;
   if (nst > 0)
     dw.load(ic, kw0, kw1, __builtin_amdgcn_readlane(my_page, 0), __builtin_amdgcn_readlane(my_page, 1), lane);
@@ -750,12 +784,15 @@ __device__ inline void decode_item(const AttnArgs& a, uint8_t* smem, const ItemC
     const int kbase = kw0 + st * kStepKeys;
     dw.store(wbuf, lane);
     asm volatile("" ::: "memory");
-    dec_scales<NB, KF, VF>(wbuf, lane, a.c);
-    if (st + 1 < nst)
-      dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, 2 * st + 2),
-              __builtin_amdgcn_readlane(my_page, 2 * st + 3), lane);
+    dec_scales<NB, KF, VF>(wbuf, lane, a.c, kw1 - kbase);
+    if (st + 1 < nst) {
+      const int run = 2 * (st + 1);
+      if ((run & 63) == 0) my_page = page_window(run >> 6);
+      dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, run & 63),
+              __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
+    }
     asm volatile("" ::: "memory");
-    dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, lane);
+    dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, kbase + kStepKeys > kw1, lane);
     asm volatile("" ::: "memory");
   }
   float lsum = gr.l;
@@ -783,23 +820,56 @@ __device__ inline void decode_item(const AttnArgs& a, uint8_t* smem, const ItemC
       Ls += ml[w * 16 + hl] * sc;
       O += mo[(w * 16 + hl) * D + dd] * sc;
     }
-    const int h = g * G + hl;
-    if (single) {
-      a.out[((int64_t)r0 * a.hq + h) * D + dd] = O / Ls;
+    if (whole) {
+      a.out[((int64_t)r0 * a.hq + g * G + hl) * D + dd] = O / Ls;
     } else {
-      const int64_t pi = pbase + hl;
-      if (pi < a.n_partials) {
-        a.o_part[pi * D + dd] = O;
-        if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
-      }
+      const int64_t pi = (int64_t)slot * G + hl;
+      a.o_part[pi * D + dd] = O;
+      if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
     }
+  }
+}
+
+// Decode work-group w: stages [w*R, min((w+1)*R, units)) of the decode stream,
+// one piece per segment it touches.  The work-group that runs a segment's
+// first stage records where the segment's results went.
+template <int NB, int KF, int VF>
+__device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
+  const TabView tv = tab_view(a);
+  const int G = a.hq / a.hkv;
+  const int x0 = w * a.dec_range, x1 = min(x0 + a.dec_range, a.dec_units);
+  int e = wave_find(tv.dec_unit, a.n_dec, x0);
+  int x = x0, k = 0;
+  while (x < x1) {
+    const int ctx = tv.dec_ctx[e], ub = tv.dec_unit[e];
+    const int nst = dec_stages(ctx);
+    const int g = (x - ub) / nst;
+    const int seg_lo = ub + g * nst, seg_hi = seg_lo + nst;
+    const int p_hi = min(x1, seg_hi);
+    const int r0 = tv.dec_r0[e];
+    const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
+    const int slot = w * a.dec_pmax + k;
+    decode_piece<NB, KF, VF>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
+                             min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
+    if (first && threadIdx.x == 0) {
+      DirEntry d;
+      d.slot = slot;
+      d.wg = w;
+      d.n = whole ? 1 : (seg_hi - 1) / a.dec_range - w + 1;
+      d.rh0 = r0 * a.hq + g * G;
+      a.dir[e * a.hkv + g] = d;
+    }
+    x = p_hi;
+    ++k;
+    if (x == seg_hi && g + 1 == a.hkv) ++e;
+    __syncthreads();  // the LDS of this piece is free again
   }
 }
 
 // Chunk tile (rows qt*R .. qt*R+R-1 of sequence s, KV head g, keys [kb, ke)).
 template <int NB, int KF, int VF>
 __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
-                                  int g, int qt, int kb, int ke, bool single, int64_t pbase) {
+                                  int g, int qt, int kb, int ke) {
   using L = DecLayout<NB, KF, VF>;
   using CL = ChunkLayout<NB, KF, VF>;
   constexpr int D = 32 * NB;
@@ -865,81 +935,47 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   if (i >= q_len) return;
   const int h = g * G + hl;
   const int q = lane >> 5;
-  if (single) {
-    const float inv = 1.f / ltot;
-    float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * q;
+  const float inv = 1.f / ltot;
+  float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * q;
 #pragma unroll
-    for (int tt = 0; tt < NB; ++tt)
+  for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
-            float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]} * inv;
-  } else {
-    const int64_t pi = pbase + (int64_t)hl * R + row_in_tile;
-    if (pi < a.n_partials) {
-      float* dst = a.o_part + pi * D + 4 * q;
-#pragma unroll
-      for (int tt = 0; tt < NB; ++tt)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
-              float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]};
-      if (q == 0) a.ml_part[pi] = make_float2(cw.m, ltot);
-    }
-  }
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
+          float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]} * inv;
 }
 
-template <int NB, int KF, int VF, bool HAS_CHUNK>
-__device__ inline void attention_body(const AttnArgs& a, uint8_t* smem, int* sh) {
-  const int tid = threadIdx.x;
-  const int item = blockIdx.x;
-  Found f;
-  if (!locate_item(a, item, f, sh)) return;
-  const int s = f.s;
-  const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
-  const int ctx = prefix + q_len;
+// Chunk work item `item`: row tile qt and KV head g of chunk entry c.
+template <int NB, int KF, int VF>
+__device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
+  const TabView tv = tab_view(a);
+  const int c = wave_find(tv.ch_item, a.n_chunk, item);
+  const int local = item - tv.ch_item[c];
+  const int r0 = tv.ch_r0[c], q_len = tv.ch_qlen[c], prefix = tv.ch_prefix[c];
   const int G = a.hq / a.hkv, R = chunk_rows(G);
-  const SeqPlan p = plan_seq(q_len, prefix, a.hkv, G);
-
-  int qt, g, j;
-  if (p.is_chunk) {
-    qt = f.local % p.n_qt;
-    const int rest = f.local / p.n_qt;
-    j = rest % p.n_split;
-    g = rest / p.n_split;
-  } else {
-    qt = 0;
-    j = f.local % p.n_split;
-    g = f.local / p.n_split;
-  }
-  if (tid == 0 && f.local == 0) a.seq_base[s] = f.item_base;
-  if (g == 0 && j == 0) {
-    const int rows = p.is_chunk ? R : 1;
-    for (int r = tid; r < rows; r += blockDim.x) {
-      const int i = qt * R + r;
-      if (i < q_len) a.row_seq[r0 + i] = s;
-    }
-  }
-  const int kb = j * p.split_len;
-  int ke = min(ctx, kb + p.split_len);
-  if (p.is_chunk) ke = min(ke, prefix + min(q_len, (qt + 1) * R));  // past the tile's last row
-  if (kb >= ke) return;  // no row of this tile sees this split
-  const int64_t pbase = partial_base(item, a.n_chunk_items, G);
-  const bool single = p.n_split == 1;
-
+  const int n_qt = ceil_div(q_len, R);
+  const int qt = local % n_qt, g = local / n_qt;
   ItemCtx ic;
   ic.k_pool = a.k_pool;
   ic.v_pool = a.v_pool;
-  ic.bt_row = a.block_table + (int64_t)s * a.max_pages;
+  ic.bt_row = a.block_table + (int64_t)tv.ch_seq[c] * a.max_pages;
   ic.hkv = a.hkv;
   ic.g = g;
   ic.page_size = a.page_size;
+  const int ke = prefix + min(q_len, (qt + 1) * R);  // keys past the tile's last row are never seen
+  chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, qt, 0, ke);
+}
 
-  if (!p.is_chunk) {
-    decode_item<NB, KF, VF>(a, smem, ic, r0, ctx, g, kb, ke, p.split_len, single, pbase);
-  } else if constexpr (HAS_CHUNK) {
-    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, qt, kb, ke, single, pbase);
+template <int NB, int KF, int VF, bool HAS_CHUNK>
+__device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
+  const int b = blockIdx.x;
+  if constexpr (HAS_CHUNK) {
+    if (b < a.n_chunk_items) {
+      chunk_work<NB, KF, VF>(a, smem, b);
+      return;
+    }
   }
+  decode_wg<NB, KF, VF>(a, smem, b - a.n_chunk_items);
 }
 
 template <int NB, int KF, int VF>
@@ -962,8 +998,7 @@ template <int NB, int KF, int VF>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 mixed_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
-  __shared__ int sh[2 * kMaxWaves + 4];
-  attention_body<NB, KF, VF, true>(a, smem, sh);
+  attention_body<NB, KF, VF, true>(a, smem);
 }
 
 // Decode-only batches: kDecodeWaves waves per work-group, at least three per SIMD.
@@ -971,69 +1006,125 @@ template <int NB, int KF, int VF>
 __global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 8)))
 decode_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF>(kDecodeWaves)];
-  __shared__ int sh[2 * kMaxWaves + 4];
-  attention_body<NB, KF, VF, false>(a, smem, sh);
+  attention_body<NB, KF, VF, false>(a, smem);
 }
 
-// Merges the split-K partials of rows whose keys span several splits.  One
-// work-group per (row, query head): the max over splits is reduced across the
-// whole group, then each thread sums a strided subset of splits for one dim
-// and the subsets are added in fixed order, so the result is deterministic.
-constexpr int kCombineThreads = 1024;
+// Merges the pieces of decode segments that span several decode work-groups.
+// One work-group per (segment, query head of the group, 32 dims): thread
+// (phase ph, dim) folds pieces ph, ph+8, ph+16, ... into a running (m, l, o)
+// with eight independent loads in flight, then the eight phases are folded in
+// phase order.  The order depends only on the piece count: deterministic.
+constexpr int kCombinePhases = 8;
+constexpr int kCombineThreads = 32 * kCombinePhases;
+constexpr int kCombineUnroll = 8;
+
+__device__ inline void lse_fold(float& m, float& l, float& o, float m2, float l2, float o2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  const float a1 = __builtin_amdgcn_exp2f(m - mn), a2 = __builtin_amdgcn_exp2f(m2 - mn);
+  l = l * a1 + l2 * a2;
+  o = o * a1 + o2 * a2;
+  m = mn;
+}
 
 __global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(AttnArgs a, int head_dim) {
-  __shared__ float red[2 * kCombineThreads];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
-  const int s = a.row_seq[row];
-  if (s < 0 || s >= a.num_seqs) return;
-  const int G = a.hq / a.hkv, R = chunk_rows(G);
-  const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
-  const SeqPlan p = plan_seq(q_len, prefix, a.hkv, G);
-  if (p.n_split == 1) return;
-  const int item_base = a.seq_base[s];
-  const int i = row - r0;
-  if (i < 0 || i >= q_len || item_base < 0 || item_base >= a.n_items) return;
-  const int nj = (prefix + i) / p.split_len + 1;
-  const int qt = i / R, rr = i % R;
-  const int g = h / G, hl = h % G;
-  auto pidx = [&](int jj) -> int64_t {
-    const int item = p.is_chunk ? item_base + qt + p.n_qt * (jj + p.n_split * g) : item_base + g * p.n_split + jj;
-    return partial_base(item, a.n_chunk_items, G) + (p.is_chunk ? (int64_t)hl * R + rr : hl);
-  };
-  float M = -INFINITY;
-  for (int jj = tid; jj < nj; jj += blockDim.x) {
-    const int64_t pi = pidx(jj);
-    if (pi >= 0 && pi < a.n_partials) M = fmaxf(M, a.ml_part[pi].x);
+  __shared__ float red[3][kCombineThreads];
+  const int G = a.hq / a.hkv, ndg = head_dim / 32;
+  const int seg = blockIdx.x / (G * ndg), rem = blockIdx.x % (G * ndg);
+  const int hl = rem / ndg, dd = (rem % ndg) * 32 + (threadIdx.x & 31);
+  const int ph = threadIdx.x >> 5;
+  const DirEntry d = a.dir[seg];
+  if (d.n <= 1) return;
+  auto slot = [&](int p) -> int64_t { return p == 0 ? d.slot : (int64_t)(d.wg + p) * a.dec_pmax; };
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int p0 = ph; p0 < d.n; p0 += kCombinePhases * kCombineUnroll) {
+    float2 ml[kCombineUnroll];
+    float ov[kCombineUnroll];
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const int p = p0 + kCombinePhases * u;
+      ml[u] = make_float2(-INFINITY, 0.f);
+      ov[u] = 0.f;
+      if (p < d.n) {
+        const int64_t pi = slot(p) * G + hl;
+        ml[u] = a.ml_part[pi];
+        ov[u] = a.o_part[pi * head_dim + dd];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) lse_fold(m, l, o, ml[u].x, ml[u].y, ov[u]);
   }
-  red[tid] = M;
+  red[0][threadIdx.x] = m;
+  red[1][threadIdx.x] = l;
+  red[2][threadIdx.x] = o;
   __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+  if (ph == 0) {
+    for (int k = 1; k < kCombinePhases; ++k) {
+      const int t = 32 * k + (threadIdx.x & 31);
+      lse_fold(m, l, o, red[0][t], red[1][t], red[2][t]);
+    }
+    a.out[((int64_t)d.rh0 + hl) * head_dim + dd] = o / l;
+  }
+}
+
+// Writes the launch-order tables to the workspace for batches too large for
+// the kernel arguments: one work-group, each thread classifies a contiguous
+// range of sequences, ranges are placed by a work-group exclusive scan.
+constexpr int kPlanThreads = 1024;
+
+__global__ void __launch_bounds__(kPlanThreads)
+plan_kernel(AttnArgs a) {
+  __shared__ int scan[4][kPlanThreads];
+  const int tid = threadIdx.x;
+  const int G = a.hq / a.hkv;
+  const int per = ceil_div(a.num_seqs, kPlanThreads);
+  const int s0 = min(a.num_seqs, tid * per), s1 = min(a.num_seqs, s0 + per);
+  int v[4] = {0, 0, 0, 0};  // decode entries, decode units, chunk entries, chunk items
+  for (int s = s0; s < s1; ++s) {
+    const int q_len = a.q_start[s + 1] - a.q_start[s], ctx = a.prefix_len[s] + q_len;
+    if (q_len > 1) { v[2] += 1; v[3] += chunk_items(q_len, a.hkv, G); }
+    else { v[0] += 1; v[1] += a.hkv * dec_stages(ctx); }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) scan[k][tid] = v[k];
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+    int t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = tid >= off ? scan[k][tid - off] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) scan[k][tid] += t[k];
     __syncthreads();
   }
-  M = red[0];
-  __syncthreads();
-  const int sgs = blockDim.x / head_dim, d = tid % head_dim, sg = tid / head_dim;
-  float O = 0.f, Ls = 0.f;
-  for (int jj = sg; jj < nj; jj += sgs) {
-    const int64_t pi = pidx(jj);
-    if (pi < 0 || pi >= a.n_partials) continue;
-    const float2 ml = a.ml_part[pi];
-    const float sc = __builtin_amdgcn_exp2f(ml.x - M);
-    Ls += ml.y * sc;
-    O += a.o_part[pi * head_dim + d] * sc;
-  }
-  red[tid] = O;
-  red[kCombineThreads + tid] = Ls;
-  __syncthreads();
-  if (sg == 0) {
-    for (int k = 1; k < sgs; ++k) {
-      O += red[k * head_dim + d];
-      Ls += red[kCombineThreads + k * head_dim + d];
+  int base[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) base[k] = scan[k][tid] - v[k];
+  const WsTabs t = ws_tabs(a.n_dec, a.n_chunk);
+  int* w = a.ws_tab;
+  for (int s = s0; s < s1; ++s) {
+    const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
+    if (q_len > 1) {
+      const int c = base[2]++;
+      w[t.ch_item + c] = base[3];
+      w[t.ch_seq + c] = s;
+      w[t.ch_r0 + c] = r0;
+      w[t.ch_qlen + c] = q_len;
+      w[t.ch_prefix + c] = prefix;
+      base[3] += chunk_items(q_len, a.hkv, G);
+    } else {
+      const int e = base[0]++;
+      w[t.dec_unit + e] = base[1];
+      w[t.dec_seq + e] = s;
+      w[t.dec_r0 + e] = r0;
+      w[t.dec_ctx + e] = prefix + 1;
+      base[1] += a.hkv * dec_stages(prefix + 1);
     }
-    a.out[((int64_t)row * a.hq + h) * head_dim + d] = O / Ls;
+  }
+  if (tid == kPlanThreads - 1) {
+    w[t.dec_unit + a.n_dec] = scan[1][tid];
+    w[t.ch_item + a.n_chunk] = scan[3][tid];
   }
 }
 
@@ -1054,8 +1145,18 @@ int check_layout(const mab_kv_layout* L) {
 }
 
 struct HostPlan {
-  int64_t n_chunk_items = 0, n_items = 0, n_partials = 0;
+  int n_dec = 0, n_chunk = 0, n_chunk_items = 0;
+  int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
+  int64_t n_slots = 0;
 };
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
 
 int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   if (!B) return MAB_ERR_NULL;
@@ -1065,27 +1166,84 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   if (!B->q_start || !B->prefix_len || !B->block_table || !B->q_start_host || !B->prefix_len_host)
     return MAB_ERR_NULL;
   if (B->q_start_host[0] != 0 || B->q_start_host[B->num_seqs] != B->num_rows) return MAB_ERR_SHAPE;
-  const int G = L->num_q_heads / L->num_kv_heads;
-  int64_t chunk = 0, dec = 0;
+  const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
+  int64_t items = 0, units = 0;
+  int n_dec = 0, n_chunk = 0;
   for (int s = 0; s < B->num_seqs; ++s) {
     const int64_t q_len = (int64_t)B->q_start_host[s + 1] - B->q_start_host[s];
     const int64_t prefix = B->prefix_len_host[s];
     if (q_len < 1 || prefix < 0) return MAB_ERR_SHAPE;
     const int64_t ctx = prefix + q_len;
     if (ctx > (int64_t)B->max_pages_per_seq * L->page_size || ctx > (int64_t)1 << 30) return MAB_ERR_SHAPE;
-    const SeqPlan p = plan_seq((int)q_len, (int)prefix, L->num_kv_heads, G);
-    if (p.is_chunk) chunk += p.items; else dec += p.items;
+    if (q_len > 1) { ++n_chunk; items += chunk_items((int)q_len, hkv, G); }
+    else { ++n_dec; units += (int64_t)hkv * dec_stages((int)ctx); }
   }
-  if (chunk + dec > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
-  if (hp) {
-    hp->n_chunk_items = chunk;
-    hp->n_items = chunk + dec;
-    hp->n_partials = chunk * G * chunk_rows(G) + dec * G;
+  if (items > (int64_t)1 << 30 || units > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
+  if (!hp) return MAB_OK;
+  hp->n_dec = n_dec;
+  hp->n_chunk = n_chunk;
+  hp->n_chunk_items = (int)items;
+  hp->dec_units = (int)units;
+  if (units > 0) {
+    // equal ranges, as many as fit on the device at once (fewer for small
+    // batches: at least kMinWGStages stages each)
+    const int64_t max_wgs = (int64_t)kDecWGsPerCU * device_cus();
+    int64_t wgs = std::min<int64_t>(max_wgs, std::max<int64_t>(1, units / kMinWGStages));
+    const int64_t range = ceil_div64(units, wgs);
+    wgs = ceil_div64(units, range);
+    hp->dec_wgs = (int)wgs;
+    hp->dec_range = (int)range;
+    // pieces per work-group: one plus the segment starts strictly inside its range
+    std::vector<int> pieces((size_t)wgs, 1);
+    int64_t x = 0;
+    for (int s = 0; s < B->num_seqs; ++s) {
+      const int q_len = B->q_start_host[s + 1] - B->q_start_host[s];
+      if (q_len > 1) continue;
+      const int nst = dec_stages(B->prefix_len_host[s] + 1);
+      for (int g = 0; g < hkv; ++g, x += nst)
+        if (x % range != 0) ++pieces[(size_t)(x / range)];
+    }
+    hp->dec_pmax = *std::max_element(pieces.begin(), pieces.end());
+    hp->n_slots = (int64_t)wgs * hp->dec_pmax;
   }
   return MAB_OK;
 }
 
+WsLayout plan_ws(const mab_kv_layout* L, const HostPlan& hp) {
+  const int G = L->num_q_heads / L->num_kv_heads;
+  const bool big = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
+  return ws_layout(hp.n_slots, G, L->head_dim, (int64_t)hp.n_dec * L->num_kv_heads,
+                   big ? ws_tabs(hp.n_dec, hp.n_chunk).total : 0);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The launch-order tables in the kernel arguments (small batches).
+void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
+  const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
+  int e = 0, c = 0, unit = 0, item = 0;
+  for (int s = 0; s < B->num_seqs; ++s) {
+    const int r0 = B->q_start_host[s], q_len = B->q_start_host[s + 1] - r0, prefix = B->prefix_len_host[s];
+    if (q_len > 1) {
+      a->tabs.ch_item[c] = item;
+      a->tabs.ch_seq[c] = s;
+      a->tabs.ch_r0[c] = r0;
+      a->tabs.ch_qlen[c] = q_len;
+      a->tabs.ch_prefix[c] = prefix;
+      item += chunk_items(q_len, hkv, G);
+      ++c;
+    } else {
+      a->tabs.dec_unit[e] = unit;
+      a->tabs.dec_seq[e] = s;
+      a->tabs.dec_r0[e] = r0;
+      a->tabs.dec_ctx[e] = prefix + 1;
+      unit += hkv * dec_stages(prefix + 1);
+      ++e;
+    }
+  }
+  a->tabs.dec_unit[e] = unit;
+  a->tabs.ch_item[c] = item;
+}
 
 template <int KF, int VF>
 void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, const void* vn, void* kp,
@@ -1137,7 +1295,7 @@ int64_t attention_workspace_bytes(const mab_kv_layout* layout, const mab_batch* 
   HostPlan hp;
   st = check_batch(layout, batch, &hp);
   if (st) return -st;
-  return ws_layout(hp.n_partials, batch->num_rows, batch->num_seqs, layout->head_dim).total;
+  return plan_ws(layout, hp).total;
 }
 
 int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch, const void* k_new,
@@ -1170,7 +1328,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   if (!q || !k_pool || !v_pool || !out || !workspace) return MAB_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
     return MAB_ERR_ALIGN;
-  const WsLayout wl = ws_layout(hp.n_partials, batch->num_rows, batch->num_seqs, layout->head_dim);
+  const WsLayout wl = plan_ws(layout, hp);
   if (workspace_bytes < wl.total) return MAB_ERR_WORKSPACE;
 
   char* ws = (char*)workspace;
@@ -1184,26 +1342,37 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   a.out = out;
   a.o_part = (float*)(ws + wl.o_off);
   a.ml_part = (float2*)(ws + wl.ml_off);
-  a.row_seq = (int32_t*)(ws + wl.row_seq_off);
-  a.seq_base = (int32_t*)(ws + wl.seq_base_off);
-  a.n_partials = hp.n_partials;
+  a.dir = (DirEntry*)(ws + wl.dir_off);
+  a.ws_tab = (int32_t*)(ws + wl.tab_off);
   a.num_seqs = batch->num_seqs;
-  a.num_rows = batch->num_rows;
   a.max_pages = batch->max_pages_per_seq;
   a.hq = layout->num_q_heads;
   a.hkv = layout->num_kv_heads;
   a.page_size = layout->page_size;
-  a.n_chunk_items = (int)hp.n_chunk_items;
-  a.n_items = (int)hp.n_items;
+  a.n_dec = hp.n_dec;
+  a.n_chunk = hp.n_chunk;
+  a.n_chunk_items = hp.n_chunk_items;
+  a.dec_units = hp.dec_units;
+  a.dec_range = hp.dec_range;
+  a.dec_pmax = hp.dec_pmax;
   a.c = sm_scale * kLog2e;
-
+  a.tabs_in_ws = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
   hipStream_t hs = (hipStream_t)stream;
-  const int grid = (int)hp.n_items;
+  if (a.tabs_in_ws) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, hs, a);
+    if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
+  } else {
+    fill_arg_tabs(layout, batch, &a);
+  }
+  const int grid = hp.n_chunk_items + hp.dec_wgs;
   if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
   else launch_attention_nb<4>(layout, a, grid, hs);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch->num_rows * layout->num_q_heads), dim3(kCombineThreads), 0,
-                     hs, a, layout->head_dim);
+  if (hp.n_dec > 0) {
+    const int G = layout->num_q_heads / layout->num_kv_heads;
+    hipLaunchKernelGGL(combine_kernel, dim3(hp.n_dec * layout->num_kv_heads * G * (layout->head_dim / 32)),
+                       dim3(kCombineThreads), 0, hs, a, layout->head_dim);
+  }
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
 

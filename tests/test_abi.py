@@ -62,23 +62,46 @@ def _ws(layout, batch):
     return mab._lib().attention_workspace_bytes(ctypes.byref(layout), ctypes.byref(batch.struct))
 
 
+def _decode_plan(ctxs, hkv, cus=256, per_cu=3, min_stages=16):
+    """The decode stream's cut, restated from its rule: the segments (one per
+    decode row and KV head, ceil(ctx/32) stages each) laid end to end, cut into
+    equal ranges, at most per_cu per compute unit and at least min_stages
+    stages each; pieces per range = 1 + segment starts strictly inside it."""
+    units = sum(hkv * -(-c // 32) for c in ctxs)
+    wgs = min(per_cu * cus, max(1, units // min_stages))
+    rng = -(-units // wgs)
+    wgs = -(-units // rng)
+    pieces = [1] * wgs
+    x = 0
+    for c in ctxs:
+        for _ in range(hkv):
+            if x % rng:
+                pieces[x // rng] += 1
+            x += -(-c // 32)
+    return wgs, rng, max(pieces)
+
+
 def test_workspace_closed_form():
     lay = mab.make_layout(24, 4, 128, 256, 1000)
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
-    # decode items: 4 heads x ceil(ctx/len), len = 2048 doubled (up to 4096) while 128*len < ctx;
-    # chunk: 2 tiles x 4 heads x 1 split, 32 rows x 6 heads each
-    def split_len(ctx):
-        n = 2048
-        while 128 * n < ctx and n < 4096:
-            n *= 2
-        return n
-    assert split_len(1001) == 2048 and split_len(70001) == 2048 and split_len(300000) == 4096
-    dec_items = 4 * (-(-1001 // 2048)) + 4 * (-(-70001 // 2048))
-    chunk_items = 2 * 4 * 1
-    partials = chunk_items * 6 * 32 + dec_items * 6
-    assert n >= partials * (128 + 2) * 4
-    assert n < partials * (128 + 2) * 4 + 4 * 256 + 8 * 4
+    wgs, rng, pmax = _decode_plan([1001, 70001], 4)
+    assert (wgs, rng, pmax) == (555, 16, 2)
+    slots = wgs * pmax
+    align = lambda x: -(-x // 256) * 256
+    o = align(slots * 6 * 128 * 4)
+    ml = align(slots * 6 * 8)
+    dirs = align(2 * 4 * 16)
+    assert n == o + ml + dirs
+
+
+def test_workspace_large_batch_holds_tables():
+    """Batches beyond the kernel-argument tables (96 decode / 16 chunk
+    sequences) keep the launch-order tables in the workspace."""
+    lay = mab.make_layout(8, 2, 64, 16, 4000)
+    small = _HostBatch(list(range(97)), [100] * 96, max_pages=16)
+    big = _HostBatch(list(range(98)), [100] * 97, max_pages=16)
+    assert _ws(lay, big) - _ws(lay, small) >= 4 * (4 * 97 + 1 + 1)
 
 
 @pytest.mark.parametrize("mutate,status", [
