@@ -39,7 +39,7 @@ constexpr int kStepKeys = 32;       // keys per stage / tile
 constexpr int kChunkSplit = 1 << 30;  // keys per chunk split (no split: a tile sees all its keys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr int kMaxSeqs = 4096;
-constexpr int kDecWGsPerCU = 3;     // decode work-groups resident per compute unit
+constexpr int kDecWGsPerCU = 2;     // decode work-groups resident per compute unit
 constexpr int kMinWGStages = 16;    // a decode work-group streams at least this many stages
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
@@ -744,7 +744,7 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
 
 // One piece of a decode segment (row r0 of sequence s, KV head g, keys
 // [kb, ke), kb a multiple of 32): the kDecodeWaves waves stream consecutive
-// ranges of 32-key stages, one stage ahead, with loads that bypass the caches'
+// ranges of 32-key stages, two stages ahead, with loads that bypass the caches'
 // retention (every byte is read once), then merge their softmax states in LDS
 // in wave order.  Any further waves of a mixed work-group sit the piece out.
 // A whole segment writes the output, a piece its partial at `slot`.
@@ -777,23 +777,33 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
   int my_page = page_window(0);
   Group<NB> gr;
   dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
-  DecWave<NB, KF, VF> dw;
-  if (nst > 0)
-    dw.load(ic, kw0, kw1, __builtin_amdgcn_readlane(my_page, 0), __builtin_amdgcn_readlane(my_page, 1), lane);
-  for (int st = 0; st < nst; ++st) {
+  // two stages in flight: stage st is consumed from one register set while
+  // stages st+1 and st+2 load into the other and into the one just freed
+  DecWave<NB, KF, VF> d0, d1;
+  auto page_of_run = [&](int run) {  // wave-uniform; run is even on every window reload
+    if (run > 0 && (run & 63) == 0) my_page = page_window(run >> 6);
+    return __builtin_amdgcn_readlane(my_page, run & 63);
+  };
+  auto issue = [&](DecWave<NB, KF, VF>& d, int st) {
+    const int run = 2 * st;
+    const int p0 = page_of_run(run);
+    d.load(ic, kw0 + st * kStepKeys, kw1, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
+  };
+  auto consume = [&](DecWave<NB, KF, VF>& d, int st) {
     const int kbase = kw0 + st * kStepKeys;
-    dw.store(wbuf, lane);
+    d.store(wbuf, lane);
     asm volatile("" ::: "memory");
     dec_scales<NB, KF, VF>(wbuf, lane, a.c, kw1 - kbase);
-    if (st + 1 < nst) {
-      const int run = 2 * (st + 1);
-      if ((run & 63) == 0) my_page = page_window(run >> 6);
-      dw.load(ic, kbase + kStepKeys, kw1, __builtin_amdgcn_readlane(my_page, run & 63),
-              __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
-    }
+    if (st + 2 < nst) issue(d, st + 2);
     asm volatile("" ::: "memory");
     dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, kbase + kStepKeys > kw1, lane);
     asm volatile("" ::: "memory");
+  };
+  if (nst > 0) issue(d0, 0);
+  if (nst > 1) issue(d1, 1);
+  for (int st = 0; st < nst; st += 2) {
+    consume(d0, st);
+    if (st + 1 < nst) consume(d1, st + 1);
   }
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
@@ -1001,9 +1011,10 @@ mixed_attention_kernel(AttnArgs a) {
   attention_body<NB, KF, VF, true>(a, smem);
 }
 
-// Decode-only batches: kDecodeWaves waves per work-group, at least three per SIMD.
+// Decode-only batches: kDecodeWaves waves per work-group, two per SIMD (room
+// for two stages in flight per wave).
 template <int NB, int KF, int VF>
-__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 decode_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF>(kDecodeWaves)];
   attention_body<NB, KF, VF, false>(a, smem);

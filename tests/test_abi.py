@@ -62,7 +62,7 @@ def _ws(layout, batch):
     return mab._lib().attention_workspace_bytes(ctypes.byref(layout), ctypes.byref(batch.struct))
 
 
-def _decode_plan(ctxs, hkv, cus=256, per_cu=3, min_stages=16):
+def _decode_plan(ctxs, hkv, cus=256, per_cu=2, min_stages=16):
     """The decode stream's cut, restated from its rule: the segments (one per
     decode row and KV head, ceil(ctx/32) stages each) laid end to end, cut into
     equal ranges, at most per_cu per compute unit and at least min_stages
@@ -86,7 +86,7 @@ def test_workspace_closed_form():
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
     wgs, rng, pmax = _decode_plan([1001, 70001], 4)
-    assert (wgs, rng, pmax) == (555, 16, 2)
+    assert (wgs, rng, pmax) == (494, 18, 2)
     slots = wgs * pmax
     align = lambda x: -(-x // 256) * 256
     o = align(slots * 6 * 128 * 4)
