@@ -34,7 +34,6 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
 constexpr int kDecodeWaves = 4;     // waves that stream a decode split (in either kernel)
-constexpr int kMaxWaves = 8;        // waves of a mixed work-group (G * ceil(4/G) <= 8)
 constexpr int kStepKeys = 32;       // keys per stage / tile
 constexpr int kChunkSplit = 1 << 30;  // keys per chunk split (no split: a tile sees all its keys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
@@ -51,19 +50,40 @@ template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static con
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves of a mixed work-group and rows of a chunk tile: every wave of a chunk
-// tile serves one query head of the group and 32 rows, so a tile has
-// 32*ceil(4/G) rows and G*ceil(4/G) waves (at least four waves per group).
-__host__ __device__ inline int mixed_waves(int group) { return group * ceil_div(4, group); }
-__host__ __device__ inline int chunk_rows(int group) { return 32 * ceil_div(4, group); }
+// A chunk tile is one work-group of kDecodeWaves = 4 waves, each serving 32
+// rows of one query head: H heads of the group (the largest of 4, 2, 1 that
+// divides G) times 128/H rows.  Its K/V steps are dequantized once for all.
+__host__ __device__ inline int chunk_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+__host__ __device__ inline int chunk_rows(int group) { return 128 / chunk_heads(group); }
 
 // A sequence with more than one row is a chunk: ceil(q_len/rows) row tiles x
-// Hkv work items.  A one-row sequence is a decode row: Hkv segments of
+// Hkv x G/H head groups, each cut into a number of key splits (one work item
+// per split).  A one-row sequence is a decode row: Hkv segments of
 // ceil(ctx/32) stages each in the decode stream.
-__host__ __device__ inline int chunk_items(int q_len, int hkv, int group) {
-  return ceil_div(q_len, chunk_rows(group)) * hkv;
+__host__ __device__ inline int chunk_tiles(int q_len, int hkv, int group) {
+  return ceil_div(q_len, chunk_rows(group)) * hkv * (group / chunk_heads(group));
 }
 __host__ __device__ inline int dec_stages(int ctx) { return ceil_div(ctx, kStepKeys); }
+
+// Key splits per tile of a chunk sequence: the F in 1..8 whose tiles*F work
+// items fill whole rounds of `slots` resident work-groups best (the smallest
+// such F).  It depends only on the sequence's own tile count and the device,
+// so a chunk row's arithmetic is the same whatever shares the batch.
+constexpr int kMaxChunkSplit = 8;
+__host__ __device__ inline int chunk_split(int tiles, int slots) {
+  int best = 1;
+  int64_t best_num = 0, best_den = 1;  // efficiency = num / den
+  for (int f = 1; f <= kMaxChunkSplit; ++f) {
+    const int64_t items = (int64_t)tiles * f;
+    const int64_t den = ((items + slots - 1) / slots) * slots;
+    if (items * best_den > best_num * den) {
+      best = f;
+      best_num = items;
+      best_den = den;
+    }
+  }
+  return best;
+}
 
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
@@ -75,20 +95,23 @@ struct DirEntry {
 };
 
 // Workspace: decode partials (slot = work-group * pmax + piece; o fp32
-// [slot][G][D], (m, l) fp32 pairs [slot][G]), one directory entry per decode
-// segment, and the launch-order tables for batches too large for the kernel
-// arguments.  Nothing needs initialising: every entry read is written first in
-// the same call.
+// [slot][G][D], (m, l) fp32 pairs [slot][G]), chunk partials of split tiles
+// (o fp32 [item][G][rows][D], (m, l) [item][G][rows]), one directory entry per
+// decode segment, and the launch-order tables for batches too large for the
+// kernel arguments.  Nothing needs initialising: every entry read is written
+// first in the same call.
 struct WsLayout {
-  int64_t o_off, ml_off, dir_off, tab_off, total;
+  int64_t o_off, ml_off, cho_off, chml_off, dir_off, tab_off, total;
 };
 
-__host__ __device__ inline WsLayout ws_layout(int64_t n_slots, int group, int head_dim, int64_t n_dec_segs,
-                                              int64_t tab_ints) {
+__host__ __device__ inline WsLayout ws_layout(int64_t n_slots, int group, int head_dim, int64_t n_chunk_rows,
+                                              int64_t n_dec_segs, int64_t tab_ints) {
   WsLayout w;
   w.o_off = 0;
   w.ml_off = align256(w.o_off + n_slots * group * head_dim * 4);
-  w.dir_off = align256(w.ml_off + n_slots * group * 8);
+  w.cho_off = align256(w.ml_off + n_slots * group * 8);
+  w.chml_off = align256(w.cho_off + n_chunk_rows * head_dim * 4);
+  w.dir_off = align256(w.chml_off + n_chunk_rows * 8);
   w.tab_off = align256(w.dir_off + n_dec_segs * (int64_t)sizeof(DirEntry));
   w.total = align256(w.tab_off + tab_ints * 4);
   return w;
@@ -263,13 +286,11 @@ __device__ inline uint32_t lds_u32(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
 }
 
-// 8 int8 codes starting at an even byte offset, as exact fp16 integers
+// 8 int8 codes (two dwords, little-endian) as exact fp16 integers
 // (magic-number conversion: 0x6400|(c^0x80) is 1152 + c in fp16).
-__device__ inline half8_t lds_codes8_q8(const uint8_t* base, int off) {
-  const int a = off & ~3, sh = off & 3;
-  const uint32_t d0 = lds_u32(base, a), d1 = lds_u32(base, a + 4), d2 = lds_u32(base, a + 8);
-  const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh) ^ 0x80808080u;
-  const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, sh) ^ 0x80808080u;
+__device__ inline half8_t codes8_q8(uint32_t w0, uint32_t w1) {
+  w0 ^= 0x80808080u;
+  w1 ^= 0x80808080u;
   const half2_t bias = {(half_t)-1152.f, (half_t)-1152.f};
   half2_t h[4];
   h[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + bias;
@@ -279,20 +300,35 @@ __device__ inline half8_t lds_codes8_q8(const uint8_t* base, int off) {
   return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
 }
 
+// Four bytes holding offset-8 nibbles (one value per byte, 0..15) as fp16 v - 8.
+__device__ inline half4_t nib4(uint32_t v) {
+  const half2_t bias = {(half_t)-1032.f, (half_t)-1032.f};
+  const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u)) + bias;
+  const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u)) + bias;
+  return half4_t{a[0], a[1], b[0], b[1]};
+}
+
+// 8 two's-complement nibbles (one dword), returned in the element order
+// (0,2,4,6,1,3,5,7) of the 8 values they encode.
+__device__ inline half8_t codes8_q4(uint32_t w) {
+  w ^= 0x88888888u;  // nibble + 8
+  const half4_t lo = nib4(w & 0x0F0F0F0Fu), hi = nib4((w >> 4) & 0x0F0F0F0Fu);
+  return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 8 int8 codes starting at an even byte offset, as exact fp16 integers.
+__device__ inline half8_t lds_codes8_q8(const uint8_t* base, int off) {
+  const int a = off & ~3, sh = off & 3;
+  const uint32_t d0 = lds_u32(base, a), d1 = lds_u32(base, a + 4), d2 = lds_u32(base, a + 8);
+  return codes8_q8(__builtin_amdgcn_alignbyte(d1, d0, sh), __builtin_amdgcn_alignbyte(d2, d1, sh));
+}
+
 // 8 two's-complement nibbles starting at an even byte offset, returned in the
 // element order (0,2,4,6,1,3,5,7) of the 8 values they encode.
 __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
   const int a = off & ~3, sh = off & 3;
   const uint32_t d0 = lds_u32(base, a), d1 = lds_u32(base, a + 4);
-  const uint32_t w = __builtin_amdgcn_alignbyte(d1, d0, sh) ^ 0x88888888u;  // nibble + 8
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  const half2_t bias = {(half_t)-1032.f, (half_t)-1032.f};
-  half2_t h[4];
-  h[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) + bias;
-  h[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) + bias;
-  h[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) + bias;
-  h[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) + bias;
-  return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+  return codes8_q4(__builtin_amdgcn_alignbyte(d1, d0, sh));
 }
 
 // Codes of value index dv (within block) for two keys at byte offsets o0, o1 of
@@ -418,7 +454,7 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
   const bool grow = mx > gr.m + kRescaleSlack;  // also true for the first keys (m = -inf)
   if (__any(grow)) {
     const float m_new = grow ? mx : gr.m;
-    const float alpha = __builtin_amdgcn_exp2f(gr.m - m_new);  // 0 when m was -inf
+    const float alpha = grow ? __builtin_amdgcn_exp2f(gr.m - m_new) : 1.f;  // 0 when m was -inf
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
     gr.l *= alpha;
@@ -460,173 +496,219 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 }
 
 // ---------------------------------------------------------------------------
-// Chunk path: each 32-key step is dequantized once into a shared LDS tile;
-// every wave serves one query head and 32 rows with 32x32x16 MFMAs.
+// Chunk path.  Every 32-key step is dequantized once into a shared LDS tile
+// (K as exact integer codes with fp32 block scales, V as fp16 values, both
+// [key][dim]); tiles are double buffered.  Each wave serves one query head and
+// 32 rows as two 16-row tiles of 16x16x32 MFMAs: S^T = K Q^T per 32-dim block
+// on integer codes, scaled per key in fp32, then O^T += V^T P^T with the V^T
+// operand read by LDS transpose reads.  A step: dequantize step s+1 from
+// registers into the other tile, issue the global loads of step s+2, compute
+// step s, one barrier.
 // ---------------------------------------------------------------------------
 
 template <int NB>
 struct ChunkTile {
   static constexpr int kD = 32 * NB;
-  static constexpr int kKStride = kD + 8;         // halves per K row (16-byte rows, skewed banks)
-  static constexpr int kVStride = kStepKeys + 4;  // halves per V^T row (72-byte rows)
-  half_t k[kStepKeys * kKStride];                 // K codes [key][dim], exact integers
-  float kd[NB * kStepKeys];                       // K scale * sm_scale*log2(e), [block][key]
-  half_t vt[kD * kVStride];                       // fp16(V code * V scale), [dim][key]
+  static constexpr int kStride = kD + 16;  // halves per key row: rows 32 bytes apart modulo 128
+  half_t k[kStepKeys * kStride];           // K codes (exact integers)
+  half_t v[kStepKeys * kStride];           // fp16(V code * scale)
+  float kd[NB * kStepKeys];                // K scale * sm_scale*log2(e), [block][key]
 };
 
-template <int NB, int KF, int VF>
-struct ChunkLayout {
-  using L = DecLayout<NB, KF, VF>;
-  static constexpr int kTileOff = ((L::kChunks * 16 + 16) + 15) / 16 * 16;  // raw stage first
-  static constexpr int kBytes = kTileOff + 2 * (int)sizeof(ChunkTile<NB>);
-  static constexpr int kLoads = (L::kChunks + 4 * 64 - 1) / (4 * 64);     // per thread, >= 4 waves
+// Position of value index e (0..31) of a block inside its LDS row segment.
+// 4-bit codes are unpacked low nibbles first, so each group of 8 values is
+// stored in the order (0,2,4,6,1,3,5,7); Q and the output follow suit.
+template <int F>
+__device__ inline int slot_of_value(int e) {
+  if constexpr (F == MAB_KV_Q8) return e;
+  else return (e & ~7) | ((e & 1) << 2) | ((e & 7) >> 1);
+}
+template <int F>
+__device__ inline int value_of_slot(int p) {
+  if constexpr (F == MAB_KV_Q8) return p;
+  else return (p & ~7) | ((p & 3) << 1) | ((p & 4) >> 2);
+}
+
+// The raw bytes of one dequant unit (the scale and 32 codes of one block of
+// one key of K or V), loaded as dwords from a 4-byte-aligned base.
+struct ChunkRaw {
+  uint32_t w[9];
+  int sh;  // byte offset of the block inside w (0 or 2)
 };
 
-// Dequantizes the raw stage into tile t: K as exact integer codes plus fp32
-// scales, V as fp16(code * scale) transposed.  Keys at or past kend become 0.
-template <int NB, int KF, int VF>
-__device__ inline void chunk_dequant(ChunkTile<NB>& t, const uint8_t* raw, int kbase, int kend, int tid, int nthr,
-                                     float zc) {
-  using L = DecLayout<NB, KF, VF>;
-  using T = ChunkTile<NB>;
-  for (int u = tid; u < kStepKeys * NB * 4; u += nthr) {
-    const int kk = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
-    const bool ok = kbase + kk < kend;
-    const int off = L::kKOff + kk * L::kRecK + b * L::kBK;
-    half8_t c = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (ok) {
-      if constexpr (KF == MAB_KV_Q8) c = lds_codes8_q8(raw, off + 2 + 8 * j);
-      else c = lds_codes8_q4(raw, off + 2 + 4 * j);  // element order (0,2,4,6,1,3,5,7)
-    }
-    *reinterpret_cast<half8_t*>(&t.k[kk * T::kKStride + 32 * b + 8 * j]) = c;
-    if (j == 0)
-      t.kd[b * kStepKeys + kk] =
-          ok ? (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(raw + off)) * zc : 0.f;
-  }
-  for (int u = tid; u < (kStepKeys / 2) * NB * 4; u += nthr) {
-    const int kp = u / (NB * 4), b = (u / 4) % NB, j = u % 4;
-    float vv[2][8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = 2 * kp + h;
-      const int off = L::kVOff + kk * L::kRecV + b * L::kBV;
-      if (kbase + kk < kend) {
-        const float d = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(raw + off));
-        half8_t c;
-        if constexpr (VF == MAB_KV_Q8) c = lds_codes8_q8(raw, off + 2 + 8 * j);
-        else c = lds_codes8_q4(raw, off + 2 + 4 * j);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vv[h][e] = (float)c[e] * d;  // exact in fp32
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vv[h][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dv = VF == MAB_KV_Q8 ? e : (e < 4 ? 2 * e : 2 * (e - 4) + 1);
-      *reinterpret_cast<half2_t*>(&t.vt[(32 * b + 8 * j + dv) * T::kVStride + 2 * kp]) =
-          half2_t{(half_t)vv[0][e], (half_t)vv[1][e]};
-    }
+template <int F>
+__device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3);
+  r.sh = (int)(addr & 3);
+  if constexpr (F == MAB_KV_Q8) {
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
+    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + 4);
+    r.w[0] = x0[0]; r.w[1] = x0[1]; r.w[2] = x0[2]; r.w[3] = x0[3];
+    r.w[4] = x1[0]; r.w[5] = x1[1]; r.w[6] = x1[2]; r.w[7] = x1[3];
+    r.w[8] = base[8];
+  } else {
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
+    r.w[0] = x0[0]; r.w[1] = x0[1]; r.w[2] = x0[2]; r.w[3] = x0[3];
+    r.w[4] = base[4];
   }
 }
 
-// One wave's chunk state: 32 slots = 32 rows of one query head.  Lane l serves
-// slot l%32; the two 32-lane halves hold different keys of S^T and different
-// dims of O^T (32x32 MFMA output layout: element e is row 8(e/4)+4(l/32)+e%4).
+// Dword m of the unit's codes (codes 4m .. 4m+3, or nibbles 8m .. 8m+7) and
+// the unit's fp16 scale bits.  The block starts at byte sh (0 or 2) of w, so
+// its codes start at byte 2 or 4: both cases use constant indices.
+__device__ inline uint32_t raw_codes(const ChunkRaw& r, int m) {
+  return r.sh ? r.w[m + 1] : __builtin_amdgcn_alignbyte(r.w[m + 1], r.w[m], 2);
+}
+__device__ inline uint32_t raw_scale(const ChunkRaw& r) { return r.sh ? r.w[0] >> 16 : r.w[0] & 0xFFFFu; }
+
+// Writes unit (key, block b) of K (is_v false) or V into tile t; an invalid
+// key (past the range) writes zeros.
+template <int NB, int KF, int VF>
+__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid,
+                                        float zc) {
+  using T = ChunkTile<NB>;
+  const int F = is_v ? VF : KF;
+  const half_t d = __builtin_bit_cast(half_t, (uint16_t)raw_scale(r));
+  half8_t out[4];
+#pragma unroll
+  for (int g8 = 0; g8 < 4; ++g8) {
+    if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes(r, 2 * g8), raw_codes(r, 2 * g8 + 1));
+    else out[g8] = codes8_q4(raw_codes(r, g8));
+    if (!valid) out[g8] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  half_t* row = (is_v ? t.v : t.k) + key * T::kStride + 32 * b;
+  if (is_v) {
+    const half8_t dv = half8_t{d, d, d, d, d, d, d, d};
+#pragma unroll
+    for (int g8 = 0; g8 < 4; ++g8) *reinterpret_cast<half8_t*>(row + 8 * g8) = out[g8] * dv;
+  } else {
+#pragma unroll
+    for (int g8 = 0; g8 < 4; ++g8) *reinterpret_cast<half8_t*>(row + 8 * g8) = out[g8];
+    t.kd[b * kStepKeys + key] = valid ? (float)d * zc : 0.f;
+  }
+}
+
+typedef _Float16 half4v_t __attribute__((ext_vector_type(4)));
+
+__device__ inline half4_t lds_tr16(const half_t* p) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  const s4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4_t*)(const_cast<half_t*>(p)));
+  return __builtin_bit_cast(half4_t, x);
+}
+
+// One wave's chunk state: two 16-row tiles of one query head.  Lane l serves
+// row l%16 of each tile; the four lanes of a row (l/16) hold different keys of
+// S^T and different dims of O^T.
 template <int NB>
 struct ChunkWave {
-  half8_t qf[NB][2];   // Q^T operand: slot l%32, dims 32b + 16c + 8(l/32) + [0,8)
-  float16_t o[NB];     // O^T per 32-dim tile
-  float m, l;          // running (possibly stale) max in log2 units; lane-partial sum
-  int limit;           // last visible key of the slot (INT_MAX for padding rows)
+  half8_t q[2][NB];    // Q^T operand: row 16*rt + l%16, block b, slots 8*(l/16) + [0,8)
+  float4_t o[2][2 * NB];  // O^T: tile rt, dim slots 16*dt + 4*(l/16) + [0,4)
+  float m[2], l[2];    // running (stale) max in log2 units; lane-partial sums
+  int limit[2];        // last visible key of the lane's row (-1 past the rows)
 };
 
 template <int NB, int KF>
-__device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* qrow, int limit, int lane) {
-  const int q = lane >> 5;
+__device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* q0, int hq, int nrows, int limit0,
+                                       int lane) {
+  const int n = lane & 15, j = lane >> 4;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = 16 * rt + n;
+    const bool ok = r < nrows;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int b = 0; b < NB; ++b) {
       half8_t v = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      if (qrow) v = *reinterpret_cast<const half8_t*>(qrow + 32 * b + 16 * c + 8 * q);
-      cw.qf[b][c] = KF == MAB_KV_Q4 ? nibble_order(v) : v;
+      if (ok) v = *reinterpret_cast<const half8_t*>(q0 + (int64_t)r * hq * (32 * NB) + 32 * b + 8 * j);
+      cw.q[rt][b] = KF == MAB_KV_Q4 ? nibble_order(v) : v;
     }
 #pragma unroll
-  for (int t = 0; t < NB; ++t) cw.o[t] = float16_t{};
-  cw.m = -INFINITY;
-  cw.l = 0.f;
-  cw.limit = qrow ? limit : 0x7fffffff;
+    for (int t = 0; t < 2 * NB; ++t) cw.o[rt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    cw.m[rt] = -INFINITY;
+    cw.l[rt] = 0.f;
+    cw.limit[rt] = ok ? limit0 + r : -1;
+  }
 }
 
+// One 32-key step of a wave on tile t (keys kbase .. kbase+31, those at or
+// past kend already zeroed).  `masked`: some key of the step lies past a row's
+// limit or past kend.
 template <int NB>
 __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int kbase, int kend, bool masked,
                                   int lane) {
   using T = ChunkTile<NB>;
-  const int q = lane >> 5, n = lane & 31;
-  float16_t s = float16_t{};
+  const int n = lane & 15, j = lane >> 4;
+  float4_t s[2][2];  // [key tile][row tile]
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float16_t pb = float16_t{};
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+    s[kt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const half_t* kr = t.k + (16 * kt + n) * T::kStride + 8 * j;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const half8_t a = *reinterpret_cast<const half8_t*>(&t.k[n * T::kKStride + 32 * b + 16 * c + 8 * q]);
-      pb = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, cw.qf[b][c], pb, 0, 0, 0);
+    for (int b = 0; b < NB; ++b) {
+      const half8_t ka = *reinterpret_cast<const half8_t*>(kr + 32 * b);
+      const float4_t kd = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, cw.q[rt][b], float4_t{0.f, 0.f, 0.f, 0.f},
+                                                                   0, 0, 0);
+        s[kt][rt] += kd * pb;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4_t kd = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 8 * i + 4 * q]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[4 * i + j] += kd[j] * pb[4 * i + j];
-    }
+    __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight (registers)
   }
-  if (masked) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kbase + 8 * (e >> 2) + 4 * q + (e & 3);
-      if (!(key <= cw.limit && key < kend)) s[e] = -INFINITY;
-    }
-  }
-  float mx = s[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-  mx = max_halves(mx);
-  const float m_new = fmaxf(cw.m, mx);
-  const bool grow = m_new > cw.m + kRescaleSlack;  // also true for the first visible key
-  if (__any(grow)) {
-    const float alpha = grow ? __builtin_amdgcn_exp2f(cw.m - m_new) : 1.f;
-#pragma unroll
-    for (int tt = 0; tt < NB; ++tt) cw.o[tt] *= alpha;
-    cw.l *= alpha;
-    if (grow) cw.m = m_new;
-  }
-  const float m_use = cw.m == -INFINITY ? 0.f : cw.m;
-  float p[16];
-  float psum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);  // <= 2^8 (stale max), masked keys 0
-    psum += p[e];
-  }
-  cw.l += psum;
   half8_t pf[2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    pf[0][e] = (half_t)p[e];
-    pf[1][e] = (half_t)p[8 + e];
-  }
+  for (int rt = 0; rt < 2; ++rt) {
+    if (masked) {
 #pragma unroll
-  for (int tt = 0; tt < NB; ++tt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      // V^T operand: dim 32tt + n; keys 16kh + 4q + [0,4) and 16kh + 8 + 4q + [0,4)
-      const half_t* vr = &t.vt[(32 * tt + n) * T::kVStride + 16 * kh + 4 * q];
-      const half4_t a0 = *reinterpret_cast<const half4_t*>(vr);
-      const half4_t a1 = *reinterpret_cast<const half4_t*>(vr + 8);
-      const half8_t vf = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      cw.o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kh], cw.o[tt], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + 16 * kt + 4 * j + i;
+          if (key > cw.limit[rt] || key >= kend) s[kt][rt][i] = -INFINITY;
+        }
     }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                     fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool grow = mx > cw.m[rt] + kRescaleSlack;  // also true for the first visible keys
+    if (__any(grow)) {
+      const float m_new = grow ? mx : cw.m[rt];
+      // 0 while m is -inf; 1 for rows whose max stands (even a row with no key yet)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(cw.m[rt] - m_new) : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < 2 * NB; ++dt) cw.o[rt][dt] *= alpha;
+      cw.l[rt] *= alpha;
+      cw.m[rt] = m_new;
+    }
+    const float m_use = cw.m[rt] == -INFINITY ? 0.f : cw.m[rt];  // rows with nothing visible yet
+    float p[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][rt][i] - m_use);  // <= 2^kRescaleSlack; masked 0
+        cw.l[rt] += p[4 * kt + i];
+      }
+    pf[rt] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
+                     (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
+  }
+  // V^T operand of dim slot 16*dt + n: keys 4j+[0,4) then 16+4j+[0,4), read by
+  // two transpose reads in which lane n names row (key 4j+n/4 (+16), slots 16dt+4(n%4)+[0,4))
+  const half_t* vr0 = t.v + (4 * j + (n >> 2)) * T::kStride + 4 * (n & 3);
+  const half_t* vr1 = vr0 + 16 * T::kStride;
+#pragma unroll
+  for (int dt = 0; dt < 2 * NB; ++dt) {
+    const half4_t a0 = lds_tr16(vr0 + 16 * dt);
+    const half4_t a1 = lds_tr16(vr1 + 16 * dt);
+    const half8_t va = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      cw.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf[rt], cw.o[rt][dt], 0, 0, 0);
+    if (dt & 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -642,7 +724,8 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 
 // Launch-order tables of the sequences.  Decode entry e (a one-row sequence):
 // its Hkv segments of dec_stages(ctx) stages each start at dec_unit[e] +
-// g*dec_stages(ctx).  Chunk entry c: work items [ch_item[c], ch_item[c+1]).
+// g*dec_stages(ctx).  Chunk entry c: work items [ch_item[c], ch_item[c+1]),
+// ch_split[c] per tile.
 // Small batches carry them in the kernel arguments; larger ones have
 // plan_kernel write them to the workspace.
 constexpr int kArgDec = 96;
@@ -651,11 +734,12 @@ constexpr int kArgChunk = 16;
 struct ArgTabs {
   int dec_unit[kArgDec + 1], dec_seq[kArgDec], dec_r0[kArgDec], dec_ctx[kArgDec];
   int ch_item[kArgChunk + 1], ch_seq[kArgChunk], ch_r0[kArgChunk], ch_qlen[kArgChunk], ch_prefix[kArgChunk];
+  int ch_split[kArgChunk];
 };
 
 // Offsets (in ints) of the tables in the workspace.
 struct WsTabs {
-  int dec_unit, dec_seq, dec_r0, dec_ctx, ch_item, ch_seq, ch_r0, ch_qlen, ch_prefix, total;
+  int dec_unit, dec_seq, dec_r0, dec_ctx, ch_item, ch_seq, ch_r0, ch_qlen, ch_prefix, ch_split, total;
 };
 
 __host__ __device__ inline WsTabs ws_tabs(int n_dec, int n_chunk) {
@@ -670,6 +754,7 @@ __host__ __device__ inline WsTabs ws_tabs(int n_dec, int n_chunk) {
   t.ch_r0 = o; o += n_chunk;
   t.ch_qlen = o; o += n_chunk;
   t.ch_prefix = o; o += n_chunk;
+  t.ch_split = o; o += n_chunk;
   t.total = o;
   return t;
 }
@@ -682,14 +767,17 @@ struct AttnArgs {
   const int32_t* prefix_len;
   const int32_t* block_table;
   float* out;
-  float* o_part;
-  float2* ml_part;
+  float* o_part;           // decode partials [slot][G][D]
+  float2* ml_part;         // [slot][G]
+  float* ch_o;             // chunk partials [item][G][rows][D]
+  float2* ch_ml;           // [item][G][rows]
   DirEntry* dir;
   int32_t* ws_tab;
   int num_seqs, max_pages;
   int hq, hkv, page_size;
   int n_dec, n_chunk;       // decode and chunk sequences
   int n_chunk_items;        // chunk work items (the first entries of the grid)
+  int ch_target;            // work-group slots the chunk splits aim to fill
   int dec_units;            // stages in the decode stream
   int dec_range;            // stages per decode work-group (the last may have fewer)
   int dec_pmax;             // partial slots per decode work-group
@@ -700,7 +788,7 @@ struct AttnArgs {
 
 struct TabView {
   const int *dec_unit, *dec_seq, *dec_r0, *dec_ctx;
-  const int *ch_item, *ch_seq, *ch_r0, *ch_qlen, *ch_prefix;
+  const int *ch_item, *ch_seq, *ch_r0, *ch_qlen, *ch_prefix, *ch_split;
 };
 
 __device__ inline TabView tab_view(const AttnArgs& a) {
@@ -711,10 +799,12 @@ __device__ inline TabView tab_view(const AttnArgs& a) {
     v.dec_unit = b + t.dec_unit; v.dec_seq = b + t.dec_seq; v.dec_r0 = b + t.dec_r0; v.dec_ctx = b + t.dec_ctx;
     v.ch_item = b + t.ch_item; v.ch_seq = b + t.ch_seq; v.ch_r0 = b + t.ch_r0; v.ch_qlen = b + t.ch_qlen;
     v.ch_prefix = b + t.ch_prefix;
+    v.ch_split = b + t.ch_split;
   } else {
     v.dec_unit = a.tabs.dec_unit; v.dec_seq = a.tabs.dec_seq; v.dec_r0 = a.tabs.dec_r0; v.dec_ctx = a.tabs.dec_ctx;
     v.ch_item = a.tabs.ch_item; v.ch_seq = a.tabs.ch_seq; v.ch_r0 = a.tabs.ch_r0; v.ch_qlen = a.tabs.ch_qlen;
     v.ch_prefix = a.tabs.ch_prefix;
+    v.ch_split = a.tabs.ch_split;
   }
   return v;
 }
@@ -747,8 +837,10 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
 // ranges of 32-key stages, two stages ahead, with loads that bypass the caches'
 // retention (every byte is read once), then merge their softmax states in LDS
 // in wave order.  Any further waves of a mixed work-group sit the piece out.
-// A whole segment writes the output, a piece its partial at `slot`.
-template <int NB, int KF, int VF>
+// A whole segment writes the output, a piece its partial at `slot`.  DEPTH:
+// stages in flight per wave (2 in the decode kernel; 1 in the mixed kernel,
+// whose chunk tiles need three waves per SIMD).
+template <int NB, int KF, int VF, int DEPTH>
 __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int r0, int ctx, int g, int kb,
                                     int ke, bool whole, int slot) {
   using L = DecLayout<NB, KF, VF>;
@@ -777,33 +869,36 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
   int my_page = page_window(0);
   Group<NB> gr;
   dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
-  // two stages in flight: stage st is consumed from one register set while
-  // stages st+1 and st+2 load into the other and into the one just freed
-  DecWave<NB, KF, VF> d0, d1;
+  // DEPTH register sets: stage st is consumed from set st % DEPTH while the
+  // next DEPTH-1 stages load into the others; its set is refilled with stage
+  // st + DEPTH as soon as it is in LDS
+  DecWave<NB, KF, VF> d[DEPTH];
   auto page_of_run = [&](int run) {  // wave-uniform; run is even on every window reload
     if (run > 0 && (run & 63) == 0) my_page = page_window(run >> 6);
     return __builtin_amdgcn_readlane(my_page, run & 63);
   };
-  auto issue = [&](DecWave<NB, KF, VF>& d, int st) {
+  auto issue = [&](DecWave<NB, KF, VF>& dw, int st) {
     const int run = 2 * st;
     const int p0 = page_of_run(run);
-    d.load(ic, kw0 + st * kStepKeys, kw1, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
+    dw.load(ic, kw0 + st * kStepKeys, kw1, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
   };
-  auto consume = [&](DecWave<NB, KF, VF>& d, int st) {
+  auto consume = [&](DecWave<NB, KF, VF>& dw, int st) {
     const int kbase = kw0 + st * kStepKeys;
-    d.store(wbuf, lane);
+    dw.store(wbuf, lane);
     asm volatile("" ::: "memory");
     dec_scales<NB, KF, VF>(wbuf, lane, a.c, kw1 - kbase);
-    if (st + 2 < nst) issue(d, st + 2);
+    if (st + DEPTH < nst) issue(dw, st + DEPTH);
     asm volatile("" ::: "memory");
     dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, kbase + kStepKeys > kw1, lane);
     asm volatile("" ::: "memory");
   };
-  if (nst > 0) issue(d0, 0);
-  if (nst > 1) issue(d1, 1);
-  for (int st = 0; st < nst; st += 2) {
-    consume(d0, st);
-    if (st + 1 < nst) consume(d1, st + 1);
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (i < nst) issue(d[i], i);
+  for (int st = 0; st < nst; st += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+      if (st + i < nst) consume(d[i], st + i);
   }
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
@@ -843,7 +938,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
 // Decode work-group w: stages [w*R, min((w+1)*R, units)) of the decode stream,
 // one piece per segment it touches.  The work-group that runs a segment's
 // first stage records where the segment's results went.
-template <int NB, int KF, int VF>
+template <int NB, int KF, int VF, int DEPTH>
 __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
   const TabView tv = tab_view(a);
   const int G = a.hq / a.hkv;
@@ -859,7 +954,7 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
     const int r0 = tv.dec_r0[e];
     const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
     const int slot = w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
+    decode_piece<NB, KF, VF, DEPTH>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
                              min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
     if (first && threadIdx.x == 0) {
       DirEntry d;
@@ -876,95 +971,116 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
   }
 }
 
-// Chunk tile (rows qt*R .. qt*R+R-1 of sequence s, KV head g, keys [kb, ke)).
+// Chunk work item: row tile qt (R rows) of a chunk sequence, KV head g, head
+// group hp (H heads), keys [kb, ke) of the rows' visible range.  Wave (hh, rg)
+// serves query head hp*H + hh of the group and rows 32*rg .. 32*rg+31 of the
+// tile.  pslot < 0: the item covers every key of its rows and writes the
+// output; otherwise its partial goes to slot pslot.
 template <int NB, int KF, int VF>
 __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
-                                  int g, int qt, int kb, int ke) {
-  using L = DecLayout<NB, KF, VF>;
-  using CL = ChunkLayout<NB, KF, VF>;
+                                  int g, int hp, int qt, int kb, int ke, int64_t pslot) {
   constexpr int D = 32 * NB;
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
-  const int G = a.hq / a.hkv, R = chunk_rows(G);
-  const int hl = wave % G, rg = wave / G;
-  uint8_t* raw = smem;
-  ChunkTile<NB>* tiles = reinterpret_cast<ChunkTile<NB>*>(smem + CL::kTileOff);
+  constexpr int kUnits = 2 * kStepKeys * NB;  // dequant units of a step: (key, block) of K, then of V
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
+  const int hh = wave % H, rg = wave / H, hl = hp * H + hh;
+  ChunkTile<NB>* tiles = reinterpret_cast<ChunkTile<NB>*>(smem);
 
-  const int row_in_tile = 32 * rg + (lane & 31);
-  const int i = qt * R + row_in_tile;
+  const int row0 = qt * R + 32 * rg;  // the wave's first row within the chunk
+  const int nrows = max(0, min(32, q_len - row0));
   ChunkWave<NB> cw;
-  chunk_wave_init<NB, KF>(cw, i < q_len ? a.q + ((int64_t)(r0 + i) * a.hq + g * G + hl) * D : nullptr, prefix + i,
+  chunk_wave_init<NB, KF>(cw, a.q + ((int64_t)(r0 + row0) * a.hq + g * G + hl) * D, a.hq, nrows, prefix + row0,
                           lane);
-  const int first_row = prefix + qt * R + 32 * rg;  // smallest limit among the wave's rows
-  const bool wave_live = qt * R + 32 * rg < q_len;
+  const int nst = ceil_div(ke - kb, kStepKeys);
 
-  const int nsteps = ceil_div(ke - kb, kStepKeys);
+  // this thread's dequant unit and its loads, one step ahead of the tile it
+  // fills; page ids one step ahead of those loads
+  const bool has_unit = tid < kUnits;
+  const bool u_is_v = tid >= kUnits / 2;
+  const int u_key = (tid % (kUnits / 2)) % kStepKeys, u_b = (tid % (kUnits / 2)) / kStepKeys;
   const int ps = a.page_size;
-  auto run_addr = [&](int key, int page, const uint8_t* pool, int rec) {
-    return pool + (((int64_t)page * ic.hkv + g) * ps + key % ps) * rec;
+  auto key_of = [&](int st) { return min(kb + st * kStepKeys + u_key, ke - 1); };  // in range
+  auto page_of = [&](int st) { return ic.bt_row[key_of(st) / ps]; };
+  ChunkRaw raw;
+  auto issue = [&](int st, int page) {
+    const int64_t tok = ((int64_t)page * ic.hkv + g) * ps + key_of(st) % ps;
+    if (u_is_v) chunk_raw_load<VF>(raw, ic.v_pool + tok * (NB * Fmt<VF>::kBytes) + u_b * Fmt<VF>::kBytes);
+    else chunk_raw_load<KF>(raw, ic.k_pool + tok * (NB * Fmt<KF>::kBytes) + u_b * Fmt<KF>::kBytes);
   };
-  u32x4_t r[CL::kLoads];
-  // raw loads of step st (keys at or past ke re-read run 0, masked later)
-  auto load = [&](int st, int page0, int page1) {
-    const int kbase = kb + st * kStepKeys, key1 = kbase + 16;
-    const bool ok1 = key1 < ke;
-    const uint8_t* k0 = run_addr(kbase, page0, ic.k_pool, L::kRecK);
-    const uint8_t* v0 = run_addr(kbase, page0, ic.v_pool, L::kRecV);
-    const uint8_t* k1 = ok1 ? run_addr(key1, page1, ic.k_pool, L::kRecK) : k0;
-    const uint8_t* v1 = ok1 ? run_addr(key1, page1, ic.v_pool, L::kRecV) : v0;
-#pragma unroll
-    for (int u = 0; u < CL::kLoads; ++u)
-      r[u] = *reinterpret_cast<const u32x4_t*>(stage_chunk<NB, KF, VF>(tid + nthr * u, k0, k1, v0, v1));
+  auto dequant = [&](int st) {
+    chunk_unit_store<NB, KF, VF>(tiles[st & 1], raw, u_is_v, u_key, u_b, kb + st * kStepKeys + u_key < ke, a.c);
   };
-  auto page_of = [&](int key) { return key < ke ? ic.bt_row[key / ps] : 0; };
-  int pg0 = page_of(kb), pg1 = page_of(kb + 16);
-  load(0, pg0, pg1);
-  pg0 = page_of(kb + kStepKeys);
-  pg1 = page_of(kb + kStepKeys + 16);
-  for (int st = 0; st < nsteps; ++st) {
+  int pg_next = 0;
+  if (has_unit && nst > 0) {
+    issue(0, page_of(0));
+    const int p1 = nst > 1 ? page_of(1) : 0;
+    dequant(0);
+    if (nst > 1) issue(1, p1);
+    if (nst > 2) pg_next = page_of(2);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
     const int kbase = kb + st * kStepKeys;
+    if (has_unit && st + 1 < nst) {
+      dequant(st + 1);
+      if (st + 2 < nst) {
+        issue(st + 2, pg_next);
+        if (st + 3 < nst) pg_next = page_of(st + 3);
+      }
+    }
+    if (nrows > 0) {
+      const bool masked = kbase + kStepKeys - 1 > prefix + row0 || kbase + kStepKeys > ke;
+      chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, lane);
+    }
+    __syncthreads();
+  }
+  if (nrows == 0) return;
+  const int n = lane & 15, j = lane >> 4;
 #pragma unroll
-    for (int u = 0; u < CL::kLoads; ++u) {
-      const int ch = tid + nthr * u;
-      if (ch < L::kChunks) *reinterpret_cast<u32x4_t*>(raw + 16 * ch) = r[u];
+  for (int rt = 0; rt < 2; ++rt) {
+    float ltot = cw.l[rt];
+    ltot += __shfl_xor(ltot, 16);
+    ltot += __shfl_xor(ltot, 32);
+    const int r = 16 * rt + n;
+    if (r >= nrows) continue;
+    const int row_in_tile = 32 * rg + r;
+    float* dst;
+    float inv = 1.f;
+    if (pslot < 0) {
+      dst = a.out + ((int64_t)(r0 + row0 + r) * a.hq + g * G + hl) * D;
+      inv = 1.f / ltot;
+    } else {
+      const int64_t pi = (pslot * H + hh) * R + row_in_tile;
+      dst = a.ch_o + pi * D;
+      if (j == 0) a.ch_ml[pi] = make_float2(cw.m[rt], ltot);
     }
-    __syncthreads();
-    if (st + 1 < nsteps) {
-      load(st + 1, pg0, pg1);
-      pg0 = page_of(kbase + 2 * kStepKeys);
-      pg1 = page_of(kbase + 2 * kStepKeys + 16);
-    }
-    ChunkTile<NB>& t = tiles[st & 1];
-    chunk_dequant<NB, KF, VF>(t, raw, kbase, ke, tid, nthr, a.c);
-    __syncthreads();
-    if (wave_live) {
-      const bool masked = kbase + kStepKeys - 1 > first_row || kbase + kStepKeys > ke;
-      chunk_step<NB>(cw, t, kbase, ke, masked, lane);
+#pragma unroll
+    for (int dt = 0; dt < 2 * NB; ++dt) {
+      const float4_t o = cw.o[rt][dt] * inv;
+      if constexpr (VF == MAB_KV_Q8) {
+        *reinterpret_cast<float4_t*>(dst + 16 * dt + 4 * j) = o;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[value_of_slot<VF>(16 * dt + 4 * j + i)] = o[i];
+      }
     }
   }
-  const float ltot = sum_halves(cw.l);
-  if (i >= q_len) return;
-  const int h = g * G + hl;
-  const int q = lane >> 5;
-  const float inv = 1.f / ltot;
-  float* dst = a.out + ((int64_t)(r0 + i) * a.hq + h) * D + 4 * q;
-#pragma unroll
-  for (int tt = 0; tt < NB; ++tt)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<float4_t*>(dst + 32 * tt + 8 * k) =
-          float4_t{cw.o[tt][4 * k], cw.o[tt][4 * k + 1], cw.o[tt][4 * k + 2], cw.o[tt][4 * k + 3]} * inv;
 }
 
-// Chunk work item `item`: row tile qt and KV head g of chunk entry c.
+// Chunk work item `item` of chunk entry c: tile (local / F) = row tile qt, KV
+// head g and head group hp, key split (local % F) of F = ch_split[c].  The visible keys of
+// the tile's rows, [0, prefix + last row + 1), are cut into F ranges of whole
+// steps.
 template <int NB, int KF, int VF>
 __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   const TabView tv = tab_view(a);
   const int c = wave_find(tv.ch_item, a.n_chunk, item);
-  const int local = item - tv.ch_item[c];
+  const int local = item - tv.ch_item[c], F = tv.ch_split[c];
   const int r0 = tv.ch_r0[c], q_len = tv.ch_qlen[c], prefix = tv.ch_prefix[c];
-  const int G = a.hq / a.hkv, R = chunk_rows(G);
-  const int n_qt = ceil_div(q_len, R);
-  const int qt = local % n_qt, g = local / n_qt;
+  const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
+  const int n_qt = ceil_div(q_len, R), n_hp = G / H;
+  const int tile = local / F, j = local % F;
+  const int qt = tile % n_qt, hp = (tile / n_qt) % n_hp, g = tile / (n_qt * n_hp);
   ItemCtx ic;
   ic.k_pool = a.k_pool;
   ic.v_pool = a.v_pool;
@@ -972,8 +1088,19 @@ __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   ic.hkv = a.hkv;
   ic.g = g;
   ic.page_size = a.page_size;
-  const int ke = prefix + min(q_len, (qt + 1) * R);  // keys past the tile's last row are never seen
-  chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, qt, 0, ke);
+  const int tile_end = prefix + min(q_len, (qt + 1) * R);  // keys past the tile's last row are never seen
+  if (F == 1) {
+    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
+    return;
+  }
+  const int len = ceil_div(ceil_div(tile_end, F), kStepKeys) * kStepKeys;
+  const int kb = min(j * len, tile_end), ke = min(kb + len, tile_end);
+  if (kb < ke) {
+    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
+  } else {  // an empty split: a neutral partial (no keys) for every row of the tile
+    const int64_t base = (int64_t)item * H * R;
+    for (int u = threadIdx.x; u < H * R; u += blockDim.x) a.ch_ml[base + u] = make_float2(-INFINITY, 0.f);
+  }
 }
 
 template <int NB, int KF, int VF, bool HAS_CHUNK>
@@ -985,7 +1112,7 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
       return;
     }
   }
-  decode_wg<NB, KF, VF>(a, smem, b - a.n_chunk_items);
+  decode_wg<NB, KF, VF, 2>(a, smem, b - a.n_chunk_items);
 }
 
 template <int NB, int KF, int VF>
@@ -998,14 +1125,15 @@ constexpr int decode_smem_bytes(int waves) {
 template <int NB, int KF, int VF>
 constexpr int mixed_smem_bytes() {
   const int dec = decode_smem_bytes<NB, KF, VF>(kDecodeWaves);
-  const int chunk = ChunkLayout<NB, KF, VF>::kBytes;
+  const int chunk = 2 * (int)sizeof(ChunkTile<NB>);
   return dec > chunk ? dec : chunk;
 }
 
-// Batches with a chunk: heavy chunk tiles and decode splits in one launch of
-// G*ceil(4/G) waves per work-group.
+// Batches with a chunk: chunk tiles and decode stream ranges in one launch of
+// kDecodeWaves-wave work-groups, two waves per SIMD (two work-groups per
+// compute unit).
 template <int NB, int KF, int VF>
-__global__ void __launch_bounds__(64 * kMaxWaves)
+__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 mixed_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
   attention_body<NB, KF, VF, true>(a, smem);
@@ -1079,6 +1207,37 @@ combine_kernel(AttnArgs a, int head_dim) {
   }
 }
 
+// Merges the key splits of chunk tiles cut into more than one split.  One
+// work-group per chunk work item; the item of split 0 of a tile merges the
+// tile: each output (head, row, dim) folds the splits in split order.
+constexpr int kChunkCombineThreads = 256;
+
+__global__ void __launch_bounds__(kChunkCombineThreads)
+chunk_combine_kernel(AttnArgs a, int head_dim) {
+  const TabView tv = tab_view(a);
+  const int item = blockIdx.x;
+  const int c = wave_find(tv.ch_item, a.n_chunk, item);
+  const int local = item - tv.ch_item[c], F = tv.ch_split[c];
+  if (F == 1 || local % F != 0) return;
+  const int r0 = tv.ch_r0[c], q_len = tv.ch_qlen[c];
+  const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
+  const int n_qt = ceil_div(q_len, R), n_hp = G / H;
+  const int tile = local / F;
+  const int qt = tile % n_qt, hp = (tile / n_qt) % n_hp, g = tile / (n_qt * n_hp);
+  for (int u = threadIdx.x; u < H * R * head_dim; u += blockDim.x) {
+    const int dd = u % head_dim, rr = (u / head_dim) % R, hh = u / (head_dim * R);
+    const int i = qt * R + rr;
+    if (i >= q_len) continue;
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int j = 0; j < F; ++j) {
+      const int64_t pi = ((int64_t)(item + j) * H + hh) * R + rr;
+      const float2 ml = a.ch_ml[pi];
+      lse_fold(m, l, o, ml.x, ml.y, ml.y > 0.f ? a.ch_o[pi * head_dim + dd] : 0.f);
+    }
+    a.out[((int64_t)(r0 + i) * a.hq + g * G + hp * H + hh) * head_dim + dd] = o / l;
+  }
+}
+
 // Writes the launch-order tables to the workspace for batches too large for
 // the kernel arguments: one work-group, each thread classifies a contiguous
 // range of sequences, ranges are placed by a work-group exclusive scan.
@@ -1094,7 +1253,11 @@ plan_kernel(AttnArgs a) {
   int v[4] = {0, 0, 0, 0};  // decode entries, decode units, chunk entries, chunk items
   for (int s = s0; s < s1; ++s) {
     const int q_len = a.q_start[s + 1] - a.q_start[s], ctx = a.prefix_len[s] + q_len;
-    if (q_len > 1) { v[2] += 1; v[3] += chunk_items(q_len, a.hkv, G); }
+    if (q_len > 1) {
+      const int tiles = chunk_tiles(q_len, a.hkv, G);
+      v[2] += 1;
+      v[3] += tiles * chunk_split(tiles, a.ch_target);
+    }
     else { v[0] += 1; v[1] += a.hkv * dec_stages(ctx); }
   }
 #pragma unroll
@@ -1123,7 +1286,9 @@ plan_kernel(AttnArgs a) {
       w[t.ch_r0 + c] = r0;
       w[t.ch_qlen + c] = q_len;
       w[t.ch_prefix + c] = prefix;
-      base[3] += chunk_items(q_len, a.hkv, G);
+      const int tiles = chunk_tiles(q_len, a.hkv, G), f = chunk_split(tiles, a.ch_target);
+      w[t.ch_split + c] = f;
+      base[3] += tiles * f;
     } else {
       const int e = base[0]++;
       w[t.dec_unit + e] = base[1];
@@ -1156,7 +1321,8 @@ int check_layout(const mab_kv_layout* L) {
 }
 
 struct HostPlan {
-  int n_dec = 0, n_chunk = 0, n_chunk_items = 0;
+  int n_dec = 0, n_chunk = 0, n_chunk_items = 0, ch_target = 1;
+  bool ch_splits = false;  // some chunk tile is cut into several splits
   int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
   int64_t n_slots = 0;
 };
@@ -1178,15 +1344,23 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     return MAB_ERR_NULL;
   if (B->q_start_host[0] != 0 || B->q_start_host[B->num_seqs] != B->num_rows) return MAB_ERR_SHAPE;
   const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
+  const int cus = device_cus();
+  const int ch_target = 2 * cus;  // resident chunk work-groups: two per compute unit
   int64_t items = 0, units = 0;
   int n_dec = 0, n_chunk = 0;
+  bool ch_splits = false;
   for (int s = 0; s < B->num_seqs; ++s) {
     const int64_t q_len = (int64_t)B->q_start_host[s + 1] - B->q_start_host[s];
     const int64_t prefix = B->prefix_len_host[s];
     if (q_len < 1 || prefix < 0) return MAB_ERR_SHAPE;
     const int64_t ctx = prefix + q_len;
     if (ctx > (int64_t)B->max_pages_per_seq * L->page_size || ctx > (int64_t)1 << 30) return MAB_ERR_SHAPE;
-    if (q_len > 1) { ++n_chunk; items += chunk_items((int)q_len, hkv, G); }
+    if (q_len > 1) {
+      const int tiles = chunk_tiles((int)q_len, hkv, G), f = chunk_split(tiles, ch_target);
+      ++n_chunk;
+      items += (int64_t)tiles * f;
+      ch_splits |= f > 1;
+    }
     else { ++n_dec; units += (int64_t)hkv * dec_stages((int)ctx); }
   }
   if (items > (int64_t)1 << 30 || units > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
@@ -1194,11 +1368,13 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->n_dec = n_dec;
   hp->n_chunk = n_chunk;
   hp->n_chunk_items = (int)items;
+  hp->ch_target = ch_target;
+  hp->ch_splits = ch_splits;
   hp->dec_units = (int)units;
   if (units > 0) {
     // equal ranges, as many as fit on the device at once (fewer for small
     // batches: at least kMinWGStages stages each)
-    const int64_t max_wgs = (int64_t)kDecWGsPerCU * device_cus();
+    const int64_t max_wgs = (int64_t)kDecWGsPerCU * cus;
     int64_t wgs = std::min<int64_t>(max_wgs, std::max<int64_t>(1, units / kMinWGStages));
     const int64_t range = ceil_div64(units, wgs);
     wgs = ceil_div64(units, range);
@@ -1223,7 +1399,8 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
 WsLayout plan_ws(const mab_kv_layout* L, const HostPlan& hp) {
   const int G = L->num_q_heads / L->num_kv_heads;
   const bool big = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
-  return ws_layout(hp.n_slots, G, L->head_dim, (int64_t)hp.n_dec * L->num_kv_heads,
+  const int64_t chunk_rows_total = hp.ch_splits ? (int64_t)hp.n_chunk_items * chunk_heads(G) * chunk_rows(G) : 0;
+  return ws_layout(hp.n_slots, G, L->head_dim, chunk_rows_total, (int64_t)hp.n_dec * L->num_kv_heads,
                    big ? ws_tabs(hp.n_dec, hp.n_chunk).total : 0);
 }
 
@@ -1241,7 +1418,9 @@ void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
       a->tabs.ch_r0[c] = r0;
       a->tabs.ch_qlen[c] = q_len;
       a->tabs.ch_prefix[c] = prefix;
-      item += chunk_items(q_len, hkv, G);
+      const int tiles = chunk_tiles(q_len, hkv, G), f = chunk_split(tiles, a->ch_target);
+      a->tabs.ch_split[c] = f;
+      item += tiles * f;
       ++c;
     } else {
       a->tabs.dec_unit[e] = unit;
@@ -1270,8 +1449,7 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 template <int NB, int KF, int VF>
 void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * mixed_waves(a.hq / a.hkv)), 0,
-                       st, a);
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
   else
     hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
 }
@@ -1353,6 +1531,8 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   a.out = out;
   a.o_part = (float*)(ws + wl.o_off);
   a.ml_part = (float2*)(ws + wl.ml_off);
+  a.ch_o = (float*)(ws + wl.cho_off);
+  a.ch_ml = (float2*)(ws + wl.chml_off);
   a.dir = (DirEntry*)(ws + wl.dir_off);
   a.ws_tab = (int32_t*)(ws + wl.tab_off);
   a.num_seqs = batch->num_seqs;
@@ -1363,6 +1543,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   a.n_dec = hp.n_dec;
   a.n_chunk = hp.n_chunk;
   a.n_chunk_items = hp.n_chunk_items;
+  a.ch_target = hp.ch_target;
   a.dec_units = hp.dec_units;
   a.dec_range = hp.dec_range;
   a.dec_pmax = hp.dec_pmax;
@@ -1379,6 +1560,11 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
   else launch_attention_nb<4>(layout, a, grid, hs);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
+  if (hp.ch_splits) {
+    hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items), dim3(kChunkCombineThreads), 0, hs, a,
+                       layout->head_dim);
+    if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
+  }
   if (hp.n_dec > 0) {
     const int G = layout->num_q_heads / layout->num_kv_heads;
     hipLaunchKernelGGL(combine_kernel, dim3(hp.n_dec * layout->num_kv_heads * G * (layout->head_dim / 32)),

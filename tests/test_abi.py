@@ -81,18 +81,38 @@ def _decode_plan(ctxs, hkv, cus=256, per_cu=2, min_stages=16):
     return wgs, rng, max(pieces)
 
 
+def _chunk_plan(q_len, hkv, group, cus=256):
+    """Chunk tiles and key splits, restated from their rule: a tile is H heads
+    (largest of 4, 2, 1 dividing G) x 128/H rows; the split F in 1..8 makes
+    tiles*F fill whole rounds of 2 work-groups per compute unit best."""
+    h = 4 if group % 4 == 0 else 2 if group % 2 == 0 else 1
+    rows = 128 // h
+    tiles = -(-q_len // rows) * hkv * (group // h)
+    slots = 2 * cus
+    best, eff = 1, 0.0
+    for f in range(1, 9):
+        e = tiles * f / (-(-(tiles * f) // slots) * slots)
+        if e > eff:
+            best, eff = f, e
+    return tiles, best, h, rows
+
+
 def test_workspace_closed_form():
     lay = mab.make_layout(24, 4, 128, 256, 1000)
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
     wgs, rng, pmax = _decode_plan([1001, 70001], 4)
     assert (wgs, rng, pmax) == (494, 18, 2)
+    tiles, f, h, rows = _chunk_plan(48, 4, 6)
+    assert (tiles, f, h, rows) == (12, 8, 2, 64)
     slots = wgs * pmax
     align = lambda x: -(-x // 256) * 256
     o = align(slots * 6 * 128 * 4)
     ml = align(slots * 6 * 8)
+    cho = align(tiles * f * h * rows * 128 * 4)
+    chml = align(tiles * f * h * rows * 8)
     dirs = align(2 * 4 * 16)
-    assert n == o + ml + dirs
+    assert n == o + ml + cho + chml + dirs
 
 
 def test_workspace_large_batch_holds_tables():
