@@ -509,10 +509,10 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 template <int NB>
 struct ChunkTile {
   static constexpr int kD = 32 * NB;
-  static constexpr int kStride = kD + 16;  // halves per key row: rows 32 bytes apart modulo 128
+  static constexpr int kStride = kD + 8;   // halves per key row: rows 16 bytes apart modulo 256
   half_t k[kStepKeys * kStride];           // K codes (exact integers)
   half_t v[kStepKeys * kStride];           // fp16(V code * scale)
-  float kd[NB * kStepKeys];                // K scale * sm_scale*log2(e), [block][key]
+  half_t kd[NB * kStepKeys];               // K block scale (exact), [block][key]
 };
 
 // Position of value index e (0..31) of a block inside its LDS row segment.
@@ -530,17 +530,16 @@ __device__ inline int value_of_slot(int p) {
 }
 
 // The raw bytes of one dequant unit (the scale and 32 codes of one block of
-// one key of K or V), loaded as dwords from a 4-byte-aligned base.
+// one key of K or V), loaded as dwords from the 4-byte-aligned address at or
+// below the block (the block starts at byte 0 or 2 of w).
 struct ChunkRaw {
   uint32_t w[9];
-  int sh;  // byte offset of the block inside w (0 or 2)
 };
 
 template <int F>
 __device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
   const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
   const uint32_t* base = reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3);
-  r.sh = (int)(addr & 3);
   if constexpr (F == MAB_KV_Q8) {
     const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
     const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + 4);
@@ -555,27 +554,29 @@ __device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
 }
 
 // Dword m of the unit's codes (codes 4m .. 4m+3, or nibbles 8m .. 8m+7) and
-// the unit's fp16 scale bits.  The block starts at byte sh (0 or 2) of w, so
-// its codes start at byte 2 or 4: both cases use constant indices.
+// the unit's fp16 scale bits.  The block starts at byte SH (0 or 2) of w, so
+// its codes start at byte 2 or 4.
+template <int SH>
 __device__ inline uint32_t raw_codes(const ChunkRaw& r, int m) {
-  return r.sh ? r.w[m + 1] : __builtin_amdgcn_alignbyte(r.w[m + 1], r.w[m], 2);
+  return SH ? r.w[m + 1] : __builtin_amdgcn_alignbyte(r.w[m + 1], r.w[m], 2);
 }
-__device__ inline uint32_t raw_scale(const ChunkRaw& r) { return r.sh ? r.w[0] >> 16 : r.w[0] & 0xFFFFu; }
+template <int SH>
+__device__ inline uint32_t raw_scale(const ChunkRaw& r) { return SH ? r.w[0] >> 16 : r.w[0] & 0xFFFFu; }
 
-// Writes unit (key, block b) of K (is_v false) or V into tile t; an invalid
-// key (past the range) writes zeros.
-template <int NB, int KF, int VF>
-__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid,
-                                        float zc) {
+// Writes unit (key, block b) of K (is_v false) or V into tile t.  A key past
+// the range (its bytes come from a valid key) gets scale 0: K logits and V
+// values of 0, never a stray NaN.
+template <int NB, int KF, int VF, int SH>
+__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid) {
   using T = ChunkTile<NB>;
   const int F = is_v ? VF : KF;
-  const half_t d = __builtin_bit_cast(half_t, (uint16_t)raw_scale(r));
+  half_t d = __builtin_bit_cast(half_t, (uint16_t)raw_scale<SH>(r));
+  if (!valid) d = (half_t)0.f;
   half8_t out[4];
 #pragma unroll
   for (int g8 = 0; g8 < 4; ++g8) {
-    if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes(r, 2 * g8), raw_codes(r, 2 * g8 + 1));
-    else out[g8] = codes8_q4(raw_codes(r, g8));
-    if (!valid) out[g8] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes<SH>(r, 2 * g8), raw_codes<SH>(r, 2 * g8 + 1));
+    else out[g8] = codes8_q4(raw_codes<SH>(r, g8));
   }
   half_t* row = (is_v ? t.v : t.k) + key * T::kStride + 32 * b;
   if (is_v) {
@@ -585,7 +586,7 @@ __device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, boo
   } else {
 #pragma unroll
     for (int g8 = 0; g8 < 4; ++g8) *reinterpret_cast<half8_t*>(row + 8 * g8) = out[g8];
-    t.kd[b * kStepKeys + key] = valid ? (float)d * zc : 0.f;
+    t.kd[b * kStepKeys + key] = d;
   }
 }
 
@@ -632,11 +633,13 @@ __device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* q0, int 
 }
 
 // One 32-key step of a wave on tile t (keys kbase .. kbase+31, those at or
-// past kend already zeroed).  `masked`: some key of the step lies past a row's
-// limit or past kend.
+// past kend zeroed).  Logits S stay in raw units (sum of block scale times the
+// integer-code dot product); c = sm_scale*log2(e) > 0 is applied inside the
+// exponent, so the running max m is in raw units too.  `masked`: some key of
+// the step lies past a row's limit or past kend.
 template <int NB>
 __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int kbase, int kend, bool masked,
-                                  int lane) {
+                                  float c, int lane) {
   using T = ChunkTile<NB>;
   const int n = lane & 15, j = lane >> 4;
   float4_t s[2][2];  // [key tile][row tile]
@@ -648,20 +651,19 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const half8_t ka = *reinterpret_cast<const half8_t*>(kr + 32 * b);
-      const float4_t kd = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
+      const half4_t kd = *reinterpret_cast<const half4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, cw.q[rt][b], float4_t{0.f, 0.f, 0.f, 0.f},
                                                                    0, 0, 0);
-        s[kt][rt] += kd * pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kt][rt][i] = __builtin_fmaf((float)kd[i], pb[i], s[kt][rt][i]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight (registers)
   }
-  half8_t pf[2];
+  if (__builtin_amdgcn_readfirstlane((int)masked)) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    if (masked) {
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -669,28 +671,32 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
           const int key = kbase + 16 * kt + 4 * j + i;
           if (key > cw.limit[rt] || key >= kend) s[kt][rt][i] = -INFINITY;
         }
-    }
+  }
+  half8_t pf[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
     float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
                      fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx > cw.m[rt] + kRescaleSlack;  // also true for the first visible keys
+    // rescale only when the max grows by more than 2^kRescaleSlack in exp2 units
+    const bool grow = mx * c > cw.m[rt] * c + kRescaleSlack;  // also true for the first visible keys
     if (__any(grow)) {
       const float m_new = grow ? mx : cw.m[rt];
       // 0 while m is -inf; 1 for rows whose max stands (even a row with no key yet)
-      const float alpha = grow ? __builtin_amdgcn_exp2f(cw.m[rt] - m_new) : 1.f;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((cw.m[rt] - m_new) * c) : 1.f;
 #pragma unroll
       for (int dt = 0; dt < 2 * NB; ++dt) cw.o[rt][dt] *= alpha;
       cw.l[rt] *= alpha;
       cw.m[rt] = m_new;
     }
-    const float m_use = cw.m[rt] == -INFINITY ? 0.f : cw.m[rt];  // rows with nothing visible yet
+    const float mc = cw.m[rt] == -INFINITY ? 0.f : cw.m[rt] * c;  // rows with nothing visible yet
     float p[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][rt][i] - m_use);  // <= 2^kRescaleSlack; masked 0
+        p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][rt][i], c, -mc));  // <= 2^slack; masked 0
         cw.l[rt] += p[4 * kt + i];
       }
     pf[rt] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
@@ -708,7 +714,6 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
       cw.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf[rt], cw.o[rt][dt], 0, 0, 0);
-    if (dt & 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -981,7 +986,8 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
                                   int g, int hp, int qt, int kb, int ke, int64_t pslot) {
   constexpr int D = 32 * NB;
   constexpr int kUnits = 2 * kStepKeys * NB;  // dequant units of a step: (key, block) of K, then of V
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
   const int hh = wave % H, rg = wave / H, hl = hp * H + hh;
   ChunkTile<NB>* tiles = reinterpret_cast<ChunkTile<NB>*>(smem);
@@ -993,30 +999,68 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
                           lane);
   const int nst = ceil_div(ke - kb, kStepKeys);
 
-  // this thread's dequant unit and its loads, one step ahead of the tile it
-  // fills; page ids one step ahead of those loads
+  // This thread's dequant unit: key tid%32 of one block of K or V.  Each wave
+  // holds two units whose blocks have the same parity, hence the same byte
+  // alignment in memory (records are a multiple of 4 bytes, blocks 34 or 18):
+  // head_dim 128: waves 0,1 K blocks {0,2},{1,3}, waves 2,3 V; head_dim 64:
+  // wave w K block w (lanes 0-31) and V block w (lanes 32-63).
+  const int half = (tid >> 5) & 1;
   const bool has_unit = tid < kUnits;
-  const bool u_is_v = tid >= kUnits / 2;
-  const int u_key = (tid % (kUnits / 2)) % kStepKeys, u_b = (tid % (kUnits / 2)) / kStepKeys;
+  const bool u_is_v = NB == 4 ? wave >= 2 : half != 0;
+  const int u_b = NB == 4 ? (wave & 1) + 2 * half : wave;
+  const int u_key = tid & 31;
   const int ps = a.page_size;
-  auto key_of = [&](int st) { return min(kb + st * kStepKeys + u_key, ke - 1); };  // in range
-  auto page_of = [&](int st) { return ic.bt_row[key_of(st) / ps]; };
+  const uint8_t* pool = u_is_v ? ic.v_pool : ic.k_pool;
+  const int rec = NB * (u_is_v ? Fmt<VF>::kBytes : Fmt<KF>::kBytes);
+  const int boff = u_b * (u_is_v ? Fmt<VF>::kBytes : Fmt<KF>::kBytes);
+  // position of a step's first key: page index q and slot r (wave-uniform),
+  // advanced 32 keys at a time without dividing
+  struct Pos { int q, r; };
+  auto advance = [&](Pos p) {
+    p.r += kStepKeys;
+    while (p.r >= ps) { p.r -= ps; ++p.q; }
+    return p;
+  };
+  // the lane's key of a step: past the range, the step's first key (valid)
+  auto lane_page_slot = [&](Pos p, int st, int& pidx, int& slot) {
+    const int t = kb + st * kStepKeys + u_key < ke ? p.r + u_key : p.r;
+    const int c = (t >= ps) + (t >= 2 * ps);
+    pidx = p.q + c;
+    slot = t - c * ps;
+  };
   ChunkRaw raw;
-  auto issue = [&](int st, int page) {
-    const int64_t tok = ((int64_t)page * ic.hkv + g) * ps + key_of(st) % ps;
-    if (u_is_v) chunk_raw_load<VF>(raw, ic.v_pool + tok * (NB * Fmt<VF>::kBytes) + u_b * Fmt<VF>::kBytes);
-    else chunk_raw_load<KF>(raw, ic.k_pool + tok * (NB * Fmt<KF>::kBytes) + u_b * Fmt<KF>::kBytes);
+  int raw_slot = 0;
+  auto issue = [&](int page) {  // the unit's own block only: the read never leaves the key's record
+    const int64_t tok = ((int64_t)page * ic.hkv + g) * ps + raw_slot;
+    if (u_is_v) chunk_raw_load<VF>(raw, pool + tok * rec + boff);
+    else chunk_raw_load<KF>(raw, pool + tok * rec + boff);
   };
+  const int sh = __builtin_amdgcn_readfirstlane((int)(reinterpret_cast<uintptr_t>(pool + boff) & 3));
   auto dequant = [&](int st) {
-    chunk_unit_store<NB, KF, VF>(tiles[st & 1], raw, u_is_v, u_key, u_b, kb + st * kStepKeys + u_key < ke, a.c);
+    const bool valid = kb + st * kStepKeys + u_key < ke;
+    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
+    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
   };
-  int pg_next = 0;
+  // pipeline: the tile of step st+1 is filled from registers during step st,
+  // whose loads were issued during step st-1 with page ids fetched during st-2
+  Pos p_page = {kb / ps, kb % ps};  // step of the next page-id fetch
+  int pidx, next_slot = 0, pg_next = 0;
+  auto fetch_page = [&](int st) {
+    lane_page_slot(p_page, st, pidx, next_slot);
+    pg_next = ic.bt_row[pidx];
+    p_page = advance(p_page);
+  };
   if (has_unit && nst > 0) {
-    issue(0, page_of(0));
-    const int p1 = nst > 1 ? page_of(1) : 0;
+    fetch_page(0);
+    raw_slot = next_slot;
+    issue(pg_next);
+    if (nst > 1) fetch_page(1);
     dequant(0);
-    if (nst > 1) issue(1, p1);
-    if (nst > 2) pg_next = page_of(2);
+    if (nst > 1) {
+      raw_slot = next_slot;
+      issue(pg_next);
+    }
+    if (nst > 2) fetch_page(2);
   }
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
@@ -1024,14 +1068,14 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     if (has_unit && st + 1 < nst) {
       dequant(st + 1);
       if (st + 2 < nst) {
-        issue(st + 2, pg_next);
-        if (st + 3 < nst) pg_next = page_of(st + 3);
+        raw_slot = next_slot;
+        issue(pg_next);
+        if (st + 3 < nst) fetch_page(st + 3);
       }
     }
-    if (nrows > 0) {
-      const bool masked = kbase + kStepKeys - 1 > prefix + row0 || kbase + kStepKeys > ke;
-      chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, lane);
-    }
+    // every wave computes (one past the last row on zero queries, written nowhere)
+    const bool masked = kbase + kStepKeys - 1 > prefix + row0 || kbase + kStepKeys > ke;
+    chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, a.c, lane);
     __syncthreads();
   }
   if (nrows == 0) return;
@@ -1052,7 +1096,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     } else {
       const int64_t pi = (pslot * H + hh) * R + row_in_tile;
       dst = a.ch_o + pi * D;
-      if (j == 0) a.ch_ml[pi] = make_float2(cw.m[rt], ltot);
+      if (j == 0) a.ch_ml[pi] = make_float2(cw.m[rt] == -INFINITY ? -INFINITY : cw.m[rt] * a.c, ltot);
     }
 #pragma unroll
     for (int dt = 0; dt < 2 * NB; ++dt) {
@@ -1513,6 +1557,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   HostPlan hp;
   st = check_batch(layout, batch, &hp);
   if (st) return st;
+  if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return MAB_ERR_UNSUPPORTED;  // logits kept unscaled
   if (batch->num_rows == 0) return MAB_OK;
   if (!q || !k_pool || !v_pool || !out || !workspace) return MAB_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))

@@ -160,6 +160,8 @@ def test_null_and_alignment_and_workspace_errors():
     assert lib.mixed_attention_fwd(L, B, d, d, d, 0.1, 0, d, 1 << 30, None) == 1
     assert lib.mixed_attention_fwd(L, B, d, d + 8, d, 0.1, d, d, 1 << 30, None) == 5
     assert lib.mixed_attention_fwd(L, B, d, d, d, 0.1, d, d, 16, None) == 4
+    for bad_scale in (0.0, -0.1, float("inf"), float("nan")):  # softmax scale must be positive, finite
+        assert lib.mixed_attention_fwd(L, B, d, d, d, bad_scale, d, d, 1 << 30, None) == 3
     nb = _HostBatch([0, 1, 2], [10, 20], dev_ptrs=False)
     assert lib.mixed_attention_fwd(L, ctypes.byref(nb.struct), d, d, d, 0.1, d, d, 1 << 30, None) == 1
     assert lib.kv_append_quant(None, B, d, d, d, d, None) == 1
