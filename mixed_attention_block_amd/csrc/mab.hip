@@ -537,9 +537,7 @@ struct ChunkRaw {
 };
 
 template <int F>
-__device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3);
+__device__ inline void chunk_raw_load_al(ChunkRaw& r, const uint32_t* base) {
   if constexpr (F == MAB_KV_Q8) {
     const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
     const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + 4);
@@ -551,6 +549,12 @@ __device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
     r.w[0] = x0[0]; r.w[1] = x0[1]; r.w[2] = x0[2]; r.w[3] = x0[3];
     r.w[4] = base[4];
   }
+}
+
+template <int F>
+__device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
+  chunk_raw_load_al<F>(r, reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3));
 }
 
 // Dword m of the unit's codes (codes 4m .. 4m+3, or nibbles 8m .. 8m+7) and
@@ -606,7 +610,8 @@ template <int NB>
 struct ChunkWave {
   half8_t q[2][NB];    // Q^T operand: row 16*rt + l%16, block b, slots 8*(l/16) + [0,8)
   float4_t o[2][2 * NB];  // O^T: tile rt, dim slots 16*dt + 4*(l/16) + [0,4)
-  float m[2], l[2];    // running (stale) max in log2 units; lane-partial sums
+  float4_t l[2];       // row sums of P, from an MFMA against ones (all four entries equal)
+  float m[2];          // running (stale) max of the raw logits
   int limit[2];        // last visible key of the lane's row (-1 past the rows)
 };
 
@@ -627,7 +632,7 @@ __device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* q0, int 
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) cw.o[rt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
     cw.m[rt] = -INFINITY;
-    cw.l[rt] = 0.f;
+    cw.l[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
     cw.limit[rt] = ok ? limit0 + r : -1;
   }
 }
@@ -662,6 +667,7 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
     }
   }
   if (__builtin_amdgcn_readfirstlane((int)masked)) {
+    __builtin_amdgcn_sched_barrier(0);  // keeps the masking a taken-or-skipped branch
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -695,12 +701,13 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][rt][i], c, -mc));  // <= 2^slack; masked 0
-        cw.l[rt] += p[4 * kt + i];
-      }
     pf[rt] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
                      (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
+    // the row sums of the fp16 P that the PV products use, on the matrix cores
+    const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    cw.l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[rt], cw.l[rt], 0, 0, 0);
   }
   // V^T operand of dim slot 16*dt + n: keys 4j+[0,4) then 16+4j+[0,4), read by
   // two transpose reads in which lane n names row (key 4j+n/4 (+16), slots 16dt+4(n%4)+[0,4))
@@ -976,6 +983,16 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
   }
 }
 
+// p, which holds the same value in every lane, as a value the compiler keeps
+// in scalar registers.
+template <typename T>
+__device__ inline const T* wave_uniform(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Chunk work item: row tile qt (R rows) of a chunk sequence, KV head g, head
 // group hp (H heads), keys [kb, ke) of the rows' visible range.  Wave (hh, rg)
 // serves query head hp*H + hh of the group and rows 32*rg .. 32*rg+31 of the
@@ -984,6 +1001,16 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
 template <int NB, int KF, int VF>
 __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
                                   int g, int hp, int qt, int kb, int ke, int64_t pslot) {
+  // every argument is the same across the work-group; say so, so that the
+  // step loop and the page walk run on the scalar unit
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  q_len = __builtin_amdgcn_readfirstlane(q_len);
+  prefix = __builtin_amdgcn_readfirstlane(prefix);
+  g = __builtin_amdgcn_readfirstlane(g);
+  hp = __builtin_amdgcn_readfirstlane(hp);
+  qt = __builtin_amdgcn_readfirstlane(qt);
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
   constexpr int D = 32 * NB;
   constexpr int kUnits = 2 * kStepKeys * NB;  // dequant units of a step: (key, block) of K, then of V
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1005,7 +1032,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   // head_dim 128: waves 0,1 K blocks {0,2},{1,3}, waves 2,3 V; head_dim 64:
   // wave w K block w (lanes 0-31) and V block w (lanes 32-63).
   const int half = (tid >> 5) & 1;
-  const bool has_unit = tid < kUnits;
+  const bool has_unit = wave < kUnits / 64;  // wave-uniform: the page walk stays scalar
   const bool u_is_v = NB == 4 ? wave >= 2 : half != 0;
   const int u_b = NB == 4 ? (wave & 1) + 2 * half : wave;
   const int u_key = tid & 31;
@@ -1013,36 +1040,64 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   const uint8_t* pool = u_is_v ? ic.v_pool : ic.k_pool;
   const int rec = NB * (u_is_v ? Fmt<VF>::kBytes : Fmt<KF>::kBytes);
   const int boff = u_b * (u_is_v ? Fmt<VF>::kBytes : Fmt<KF>::kBytes);
-  // position of a step's first key: page index q and slot r (wave-uniform),
-  // advanced 32 keys at a time without dividing
+  // byte offset of the unit's block in its dword (the same for every lane of a
+  // wave: records are a multiple of 4 bytes, pools 16-byte aligned)
+  const int sh = __builtin_amdgcn_readfirstlane(boff & 3);
+  ChunkRaw raw;
+  auto dequant = [&](int st) {
+    const bool valid = kb + st * kStepKeys + u_key < ke;
+    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
+    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
+  };
+  // The loads of a step.  Page sizes that are a multiple of 32 keep every step
+  // (which starts at a multiple of 32) inside one page: a wave-uniform page
+  // walk (scalar page ids, the next page's id fetched a page ahead) and a
+  // fixed per-lane offset.  Lanes past the range read bytes of the same page
+  // and are zeroed by their scale.  Other page sizes take a per-lane walk.
+  const bool uniform = ps % kStepKeys == 0;
+  const uint32_t lane_off = (uint32_t)(u_key * rec + (boff & ~3));
+  int u_q = kb / ps, u_r = kb % ps;  // page index and slot of the next step to load
+  const int q_last = (ke - 1) / ps;
+  // the block table is read-only during the call: scalar loads
+  const __attribute__((address_space(4))) int32_t* bt_const =
+      (const __attribute__((address_space(4))) int32_t*)(wave_uniform(ic.bt_row));
+  int u_pg = 0, u_pg_next = 0;
+  auto issue_uniform = [&]() {
+    const uint8_t* base = pool + (((int64_t)u_pg * ic.hkv + g) * ps + u_r) * rec;
+    if (u_is_v) chunk_raw_load_al<VF>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
+    else chunk_raw_load_al<KF>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
+    u_r += kStepKeys;
+    if (u_r == ps) {
+      u_r = 0;
+      ++u_q;
+      u_pg = u_pg_next;
+      u_pg_next = u_q < q_last ? bt_const[u_q + 1] : 0;
+    }
+  };
+  // per-lane walk: position of a step's first key (page index q, slot r),
+  // advanced 32 keys at a time without dividing; a lane past the range reads
+  // the step's first key
   struct Pos { int q, r; };
   auto advance = [&](Pos p) {
     p.r += kStepKeys;
     while (p.r >= ps) { p.r -= ps; ++p.q; }
     return p;
   };
-  // the lane's key of a step: past the range, the step's first key (valid)
   auto lane_page_slot = [&](Pos p, int st, int& pidx, int& slot) {
     const int t = kb + st * kStepKeys + u_key < ke ? p.r + u_key : p.r;
     const int c = (t >= ps) + (t >= 2 * ps);
     pidx = p.q + c;
     slot = t - c * ps;
   };
-  ChunkRaw raw;
   int raw_slot = 0;
-  auto issue = [&](int page) {  // the unit's own block only: the read never leaves the key's record
+  auto issue_lane = [&](int page) {  // the unit's own block only: the read never leaves the key's record
     const int64_t tok = ((int64_t)page * ic.hkv + g) * ps + raw_slot;
     if (u_is_v) chunk_raw_load<VF>(raw, pool + tok * rec + boff);
     else chunk_raw_load<KF>(raw, pool + tok * rec + boff);
   };
-  const int sh = __builtin_amdgcn_readfirstlane((int)(reinterpret_cast<uintptr_t>(pool + boff) & 3));
-  auto dequant = [&](int st) {
-    const bool valid = kb + st * kStepKeys + u_key < ke;
-    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
-    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
-  };
   // pipeline: the tile of step st+1 is filled from registers during step st,
-  // whose loads were issued during step st-1 with page ids fetched during st-2
+  // whose loads were issued during step st-1 (per-lane walk: with page ids
+  // fetched during st-2)
   Pos p_page = {kb / ps, kb % ps};  // step of the next page-id fetch
   int pidx, next_slot = 0, pg_next = 0;
   auto fetch_page = [&](int st) {
@@ -1050,28 +1105,32 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     pg_next = ic.bt_row[pidx];
     p_page = advance(p_page);
   };
-  if (has_unit && nst > 0) {
-    fetch_page(0);
-    raw_slot = next_slot;
-    issue(pg_next);
-    if (nst > 1) fetch_page(1);
-    dequant(0);
-    if (nst > 1) {
+  auto issue = [&](int st) {  // loads of step st (issued in step order)
+    if (uniform) {
+      issue_uniform();
+    } else {
       raw_slot = next_slot;
-      issue(pg_next);
+      issue_lane(pg_next);
+      if (st + 1 < nst) fetch_page(st + 1);
     }
-    if (nst > 2) fetch_page(2);
+  };
+  if (has_unit && nst > 0) {
+    if (uniform) {
+      u_pg = bt_const[u_q];
+      u_pg_next = u_q < q_last ? bt_const[u_q + 1] : 0;
+    } else {
+      fetch_page(0);
+    }
+    issue(0);
+    dequant(0);
+    if (nst > 1) issue(1);
   }
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     const int kbase = kb + st * kStepKeys;
     if (has_unit && st + 1 < nst) {
       dequant(st + 1);
-      if (st + 2 < nst) {
-        raw_slot = next_slot;
-        issue(pg_next);
-        if (st + 3 < nst) fetch_page(st + 3);
-      }
+      if (st + 2 < nst) issue(st + 2);
     }
     // every wave computes (one past the last row on zero queries, written nowhere)
     const bool masked = kbase + kStepKeys - 1 > prefix + row0 || kbase + kStepKeys > ke;
@@ -1082,9 +1141,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   const int n = lane & 15, j = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float ltot = cw.l[rt];
-    ltot += __shfl_xor(ltot, 16);
-    ltot += __shfl_xor(ltot, 32);
+    const float ltot = cw.l[rt][0];
     const int r = 16 * rt + n;
     if (r >= nrows) continue;
     const int row_in_tile = 32 * rg + r;
