@@ -33,13 +33,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
-constexpr int kDecodeWaves = 4;     // waves that stream a decode split (in either kernel)
+constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two work-groups per CU)
+constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
 constexpr int kStepKeys = 32;       // keys per stage / tile
 constexpr int kChunkSplit = 1 << 30;  // keys per chunk split (no split: a tile sees all its keys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr int kMaxSeqs = 4096;
-constexpr int kDecWGsPerCU = 2;     // decode work-groups resident per compute unit
-constexpr int kMinWGStages = 16;    // a decode work-group streams at least this many stages
+constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this many stages per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
 
@@ -50,11 +50,11 @@ template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static con
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// A chunk tile is one work-group of kDecodeWaves = 4 waves, each serving 32
+// A chunk tile is one work-group of kMixedWaves = 8 waves, each serving 32
 // rows of one query head: H heads of the group (the largest of 4, 2, 1 that
-// divides G) times 128/H rows.  Its K/V steps are dequantized once for all.
+// divides G) times 256/H rows.  Its K/V steps are dequantized once for all.
 __host__ __device__ inline int chunk_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
-__host__ __device__ inline int chunk_rows(int group) { return 128 / chunk_heads(group); }
+__host__ __device__ inline int chunk_rows(int group) { return 32 * kMixedWaves / chunk_heads(group); }
 
 // A sequence with more than one row is a chunk: ceil(q_len/rows) row tiles x
 // Hkv x G/H head groups, each cut into a number of key splits (one work item
@@ -247,6 +247,19 @@ __device__ inline half8_t nibble_order(half8_t q) {
 __device__ inline float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
 __device__ inline float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
+// Max over lanes l and l^16 (l^32): the row-swap instructions put the values
+// of both lanes of a pair into the two results, in either order.
+__device__ inline float max_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float max_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
 
 // ---------------------------------------------------------------------------
 // Raw stage: the bytes of 32 keys of one KV head, K then V, each as two
@@ -648,6 +661,9 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
   using T = ChunkTile<NB>;
   const int n = lane & 15, j = lane >> 4;
   float4_t s[2][2];  // [key tile][row tile]
+  // the QK products at a raised issue priority: the matrix cores get fed while
+  // the other wave of the SIMD is in its softmax or dequantization
+  __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     s[kt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -666,6 +682,7 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   if (__builtin_amdgcn_readfirstlane((int)masked)) {
     __builtin_amdgcn_sched_barrier(0);  // keeps the masking a taken-or-skipped branch
 #pragma unroll
@@ -683,8 +700,7 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
   for (int rt = 0; rt < 2; ++rt) {
     float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
                      fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     // rescale only when the max grows by more than 2^kRescaleSlack in exp2 units
     const bool grow = mx * c > cw.m[rt] * c + kRescaleSlack;  // also true for the first visible keys
     if (__any(grow)) {
@@ -845,20 +861,18 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
 }
 
 // One piece of a decode segment (row r0 of sequence s, KV head g, keys
-// [kb, ke), kb a multiple of 32): the kDecodeWaves waves stream consecutive
-// ranges of 32-key stages, two stages ahead, with loads that bypass the caches'
-// retention (every byte is read once), then merge their softmax states in LDS
-// in wave order.  Any further waves of a mixed work-group sit the piece out.
-// A whole segment writes the output, a piece its partial at `slot`.  DEPTH:
-// stages in flight per wave (2 in the decode kernel; 1 in the mixed kernel,
-// whose chunk tiles need three waves per SIMD).
-template <int NB, int KF, int VF, int DEPTH>
+// [kb, ke), kb a multiple of 32): the NW waves of the work-group stream
+// consecutive ranges of 32-key stages, DEPTH stages ahead, with loads that
+// bypass the caches' retention (every byte is read once), then merge their
+// softmax states in LDS in wave order.  A whole segment writes the output, a
+// piece its partial at `slot`.
+template <int NB, int KF, int VF, int DEPTH, int NW>
 __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int r0, int ctx, int g, int kb,
                                     int ke, bool whole, int slot) {
   using L = DecLayout<NB, KF, VF>;
   constexpr int D = 32 * NB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int nw = kDecodeWaves;
+  constexpr int nw = NW;
   const int G = a.hq / a.hkv;
   uint8_t* wbuf = smem + min(wave, nw - 1) * L::kWaveBytes;
   const int n = lane & 15;
@@ -950,7 +964,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
 // Decode work-group w: stages [w*R, min((w+1)*R, units)) of the decode stream,
 // one piece per segment it touches.  The work-group that runs a segment's
 // first stage records where the segment's results went.
-template <int NB, int KF, int VF, int DEPTH>
+template <int NB, int KF, int VF, int DEPTH, int NW>
 __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
   const TabView tv = tab_view(a);
   const int G = a.hq / a.hkv;
@@ -966,7 +980,7 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
     const int r0 = tv.dec_r0[e];
     const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
     const int slot = w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF, DEPTH>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
+    decode_piece<NB, KF, VF, DEPTH, NW>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
                              min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
     if (first && threadIdx.x == 0) {
       DirEntry d;
@@ -1030,7 +1044,8 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   // holds two units whose blocks have the same parity, hence the same byte
   // alignment in memory (records are a multiple of 4 bytes, blocks 34 or 18):
   // head_dim 128: waves 0,1 K blocks {0,2},{1,3}, waves 2,3 V; head_dim 64:
-  // wave w K block w (lanes 0-31) and V block w (lanes 32-63).
+  // wave w K block w (lanes 0-31) and V block w (lanes 32-63).  The other
+  // waves only compute (waves w and w+4 share a SIMD).
   const int half = (tid >> 5) & 1;
   const bool has_unit = wave < kUnits / 64;  // wave-uniform: the page walk stays scalar
   const bool u_is_v = NB == 4 ? wave >= 2 : half != 0;
@@ -1213,7 +1228,7 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
       return;
     }
   }
-  decode_wg<NB, KF, VF, 2>(a, smem, b - a.n_chunk_items);
+  decode_wg<NB, KF, VF, 2, HAS_CHUNK ? kMixedWaves : kDecodeWaves>(a, smem, b - a.n_chunk_items);
 }
 
 template <int NB, int KF, int VF>
@@ -1225,16 +1240,16 @@ constexpr int decode_smem_bytes(int waves) {
 
 template <int NB, int KF, int VF>
 constexpr int mixed_smem_bytes() {
-  const int dec = decode_smem_bytes<NB, KF, VF>(kDecodeWaves);
+  const int dec = decode_smem_bytes<NB, KF, VF>(kMixedWaves);
   const int chunk = 2 * (int)sizeof(ChunkTile<NB>);
   return dec > chunk ? dec : chunk;
 }
 
 // Batches with a chunk: chunk tiles and decode stream ranges in one launch of
-// kDecodeWaves-wave work-groups, two waves per SIMD (two work-groups per
+// kMixedWaves-wave work-groups, two waves per SIMD (one work-group per
 // compute unit).
 template <int NB, int KF, int VF>
-__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ void __launch_bounds__(64 * kMixedWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 mixed_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
   attention_body<NB, KF, VF, true>(a, smem);
@@ -1446,7 +1461,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   if (B->q_start_host[0] != 0 || B->q_start_host[B->num_seqs] != B->num_rows) return MAB_ERR_SHAPE;
   const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
   const int cus = device_cus();
-  const int ch_target = 2 * cus;  // resident chunk work-groups: two per compute unit
+  const int ch_target = cus;  // resident chunk work-groups: one per compute unit
   int64_t items = 0, units = 0;
   int n_dec = 0, n_chunk = 0;
   bool ch_splits = false;
@@ -1474,9 +1489,13 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->dec_units = (int)units;
   if (units > 0) {
     // equal ranges, as many as fit on the device at once (fewer for small
-    // batches: at least kMinWGStages stages each)
-    const int64_t max_wgs = (int64_t)kDecWGsPerCU * cus;
-    int64_t wgs = std::min<int64_t>(max_wgs, std::max<int64_t>(1, units / kMinWGStages));
+    // batches: at least kMinWaveStages stages per wave each); decode-only
+    // batches run two 4-wave work-groups per compute unit, mixed ones one
+    // 8-wave work-group
+    const bool mixed = n_chunk > 0;
+    const int64_t max_wgs = (int64_t)(mixed ? 1 : 2) * cus;
+    const int64_t min_stages = (int64_t)kMinWaveStages * (mixed ? kMixedWaves : kDecodeWaves);
+    int64_t wgs = std::min<int64_t>(max_wgs, std::max<int64_t>(1, units / min_stages));
     const int64_t range = ceil_div64(units, wgs);
     wgs = ceil_div64(units, range);
     hp->dec_wgs = (int)wgs;
@@ -1550,7 +1569,7 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 template <int NB, int KF, int VF>
 void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kMixedWaves), 0, st, a);
   else
     hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
 }

@@ -66,7 +66,9 @@ def _decode_plan(ctxs, hkv, cus=256, per_cu=2, min_stages=16):
     """The decode stream's cut, restated from its rule: the segments (one per
     decode row and KV head, ceil(ctx/32) stages each) laid end to end, cut into
     equal ranges, at most per_cu per compute unit and at least min_stages
-    stages each; pieces per range = 1 + segment starts strictly inside it."""
+    stages each (4 per wave: decode-only batches run two 4-wave work-groups
+    per compute unit, batches with a chunk one 8-wave work-group); pieces per
+    range = 1 + segment starts strictly inside it."""
     units = sum(hkv * -(-c // 32) for c in ctxs)
     wgs = min(per_cu * cus, max(1, units // min_stages))
     rng = -(-units // wgs)
@@ -83,12 +85,12 @@ def _decode_plan(ctxs, hkv, cus=256, per_cu=2, min_stages=16):
 
 def _chunk_plan(q_len, hkv, group, cus=256):
     """Chunk tiles and key splits, restated from their rule: a tile is H heads
-    (largest of 4, 2, 1 dividing G) x 128/H rows; the split F in 1..8 makes
-    tiles*F fill whole rounds of 2 work-groups per compute unit best."""
+    (largest of 4, 2, 1 dividing G) x 256/H rows; the split F in 1..8 makes
+    tiles*F fill whole rounds of one work-group per compute unit best."""
     h = 4 if group % 4 == 0 else 2 if group % 2 == 0 else 1
-    rows = 128 // h
+    rows = 256 // h
     tiles = -(-q_len // rows) * hkv * (group // h)
-    slots = 2 * cus
+    slots = cus
     best, eff = 1, 0.0
     for f in range(1, 9):
         e = tiles * f / (-(-(tiles * f) // slots) * slots)
@@ -101,10 +103,10 @@ def test_workspace_closed_form():
     lay = mab.make_layout(24, 4, 128, 256, 1000)
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
-    wgs, rng, pmax = _decode_plan([1001, 70001], 4)
-    assert (wgs, rng, pmax) == (494, 18, 2)
+    wgs, rng, pmax = _decode_plan([1001, 70001], 4, per_cu=1, min_stages=32)  # a batch with a chunk
+    assert (wgs, rng, pmax) == (254, 35, 2)
     tiles, f, h, rows = _chunk_plan(48, 4, 6)
-    assert (tiles, f, h, rows) == (12, 8, 2, 64)
+    assert (tiles, f, h, rows) == (12, 8, 2, 128)
     slots = wgs * pmax
     align = lambda x: -(-x // 256) * 256
     o = align(slots * 6 * 128 * 4)

@@ -93,10 +93,12 @@ def test_run_to_run_bitwise():
 def test_mixed_equals_separate(key):
     """One mixed launch versus launches of its parts.  Chunk rows are computed
     by work items that depend only on their own sequence: bitwise equal.  Decode
-    rows are cut into stream ranges that depend on the whole batch, so only the
-    summation order and the fp16 rounding of P differ: equal to 5e-4 (8x inside
-    the oracle tolerance), and each within
-    the oracle tolerance (checked by the other tests)."""
+    rows are cut into stream ranges that depend on the whole batch (and run on
+    8-wave work-groups in a mixed launch, 4-wave ones in a decode-only launch),
+    so the per-wave maxima that P and P*scale are rounded to fp16 against
+    differ, as does the summation order: equal to 1e-3 (a quarter of the oracle
+    tolerance), and each within the oracle tolerance (checked by the other
+    tests)."""
     case = _case(key)
     st = GpuState(case)
     st.append_step()
@@ -113,7 +115,8 @@ def test_mixed_equals_separate(key):
             if case.q_len(s) > 1:
                 assert np.array_equal(part[r_part], full[r_full]), f"chunk seq {s} of {seqs}"
             else:
-                assert np.abs(part[r_part] - full[r_full]).max() <= 5e-4, f"decode seq {s} of {seqs}"
+                d = float(np.abs(part[r_part] - full[r_full]).max())
+                assert d <= 1e-3, f"decode seq {s} of {seqs}: {d:.3g}"
 
 
 BOUNDARY_SEQS = [(0, 1), (1, 1), (30, 1), (31, 1), (32, 1), (510, 1), (511, 1), (512, 1),
@@ -137,7 +140,8 @@ def test_large_batch_tables_in_workspace():
     """More decode (> 96) and chunk (> 16) sequences than the kernel arguments
     hold: the launch-order tables are built on the device (plan_kernel); the
     outputs must still match the oracle, and a single decode row must match
-    its own launch to 5e-4 (different cuts round P differently)."""
+    its own launch to 1e-3 (different cuts and work-group sizes round P
+    differently)."""
     rng = np.random.default_rng(41)
     seqs = [(int(rng.integers(0, 400)), 1) for _ in range(110)]
     seqs += [(int(rng.integers(0, 200)), int(rng.integers(2, 24))) for _ in range(20)]
@@ -153,7 +157,8 @@ def test_large_batch_tables_in_workspace():
     s = next(i for i in range(case.num_seqs) if case.q_len(i) == 1 and case.prefix_len[i] > 64)
     sub, rows = synth.subset(case, [s])
     one = st.attention(batch=batch_of(sub.q_start, sub.prefix_len, sub.block_table), q=sub.q).cpu().numpy()
-    assert np.abs(one - out[rows]).max() <= 5e-4
+    d = float(np.abs(one - out[rows]).max())
+    assert d <= 1e-3, f"single decode row vs the large batch: {d:.3g}"
 
 
 def _sweep_values(gen, n, hkv, d, kind):
