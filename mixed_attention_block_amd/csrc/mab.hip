@@ -1323,15 +1323,22 @@ combine_kernel(AttnArgs a, int head_dim) {
   }
 }
 
-// Merges the key splits of chunk tiles cut into more than one split.  One
-// work-group per chunk work item; the item of split 0 of a tile merges the
-// tile: each output (head, row, dim) folds the splits in split order.
+// Merges the key splits of chunk tiles cut into more than one split.  A tile
+// holds H*R = 32*kMixedWaves rows (all its heads); work-group (item, part)
+// merges rows [part*RB, (part+1)*RB) of the tile if item is the tile's split 0
+// (the others exit at once): thread (row, 4 dims) takes the global max of the
+// splits' maxima, then sums the weighted partials in split order, with every
+// split's loads in flight together.  Deterministic.
 constexpr int kChunkCombineThreads = 256;
+__host__ __device__ inline int chunk_combine_parts(int head_dim) {
+  return 32 * kMixedWaves / (kChunkCombineThreads / (head_dim / 4));
+}
 
 __global__ void __launch_bounds__(kChunkCombineThreads)
 chunk_combine_kernel(AttnArgs a, int head_dim) {
   const TabView tv = tab_view(a);
-  const int item = blockIdx.x;
+  const int parts = chunk_combine_parts(head_dim);
+  const int item = blockIdx.x / parts, part = blockIdx.x % parts;
   const int c = wave_find(tv.ch_item, a.n_chunk, item);
   const int local = item - tv.ch_item[c], F = tv.ch_split[c];
   if (F == 1 || local % F != 0) return;
@@ -1340,18 +1347,31 @@ chunk_combine_kernel(AttnArgs a, int head_dim) {
   const int n_qt = ceil_div(q_len, R), n_hp = G / H;
   const int tile = local / F;
   const int qt = tile % n_qt, hp = (tile / n_qt) % n_hp, g = tile / (n_qt * n_hp);
-  for (int u = threadIdx.x; u < H * R * head_dim; u += blockDim.x) {
-    const int dd = u % head_dim, rr = (u / head_dim) % R, hh = u / (head_dim * R);
-    const int i = qt * R + rr;
-    if (i >= q_len) continue;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int j = 0; j < F; ++j) {
-      const int64_t pi = ((int64_t)(item + j) * H + hh) * R + rr;
-      const float2 ml = a.ch_ml[pi];
-      lse_fold(m, l, o, ml.x, ml.y, ml.y > 0.f ? a.ch_o[pi * head_dim + dd] : 0.f);
-    }
-    a.out[((int64_t)(r0 + i) * a.hq + g * G + hp * H + hh) * head_dim + dd] = o / l;
+  const int tpr = head_dim / 4;                           // threads per row
+  const int rt = part * (kChunkCombineThreads / tpr) + threadIdx.x / tpr;  // row of the tile, head-major
+  const int hh = rt / R, rr = rt % R, dd = 4 * (threadIdx.x % tpr);
+  const int i = qt * R + rr;
+  if (i >= q_len) return;
+  float2 ml[kMaxChunkSplit];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxChunkSplit; ++j) {
+    ml[j] = make_float2(-INFINITY, 0.f);
+    if (j < F) ml[j] = a.ch_ml[((int64_t)(item + j) * H + hh) * R + rr];
+    mx = fmaxf(mx, ml[j].x);
   }
+  float l = 0.f;
+  float4_t o = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxChunkSplit; ++j) {
+    if (j < F && ml[j].y > 0.f) {  // an empty split (no keys) has l = 0 and unwritten o
+      const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
+      const int64_t pi = ((int64_t)(item + j) * H + hh) * R + rr;
+      l += w * ml[j].y;
+      o += w * *reinterpret_cast<const float4_t*>(a.ch_o + pi * head_dim + dd);
+    }
+  }
+  *reinterpret_cast<float4_t*>(a.out + ((int64_t)(r0 + i) * a.hq + g * G + hp * H + hh) * head_dim + dd) = o / l;
 }
 
 // Writes the launch-order tables to the workspace for batches too large for
@@ -1682,8 +1702,8 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   else launch_attention_nb<4>(layout, a, grid, hs);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   if (hp.ch_splits) {
-    hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items), dim3(kChunkCombineThreads), 0, hs, a,
-                       layout->head_dim);
+    hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * chunk_combine_parts(layout->head_dim)),
+                       dim3(kChunkCombineThreads), 0, hs, a, layout->head_dim);
     if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   }
   if (hp.n_dec > 0) {
