@@ -88,13 +88,13 @@ __host__ __device__ inline int chunk_split(int tiles, int slots) {
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Where a decode segment's results went: its first piece's partial slot, the
-// decode work-group that ran that piece, the number of pieces (1: the output
-// was written directly) and the segment's first output row-head.
+// decode worker (wave) that ran that piece, the number of pieces (1: the
+// output was written directly) and the segment's first output row-head.
 struct DirEntry {
   int slot, wg, n, rh0;
 };
 
-// Workspace: decode partials (slot = work-group * pmax + piece; o fp32
+// Workspace: decode partials (slot = worker * pmax + piece; o fp32
 // [slot][G][D], (m, l) fp32 pairs [slot][G]), chunk partials of split tiles
 // (o fp32 [item][G][rows][D], (m, l) [item][G][rows]), one directory entry per
 // decode segment, and the launch-order tables for batches too large for the
@@ -744,10 +744,11 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
 // Launch plan.  The grid holds the chunk work items first (one work-group per
 // row tile and KV head), then the decode stream: the stages of every decode
 // segment (one decode row and KV head) laid end to end, cut into equal
-// contiguous ranges, one per decode work-group, so every work-group streams
-// the same number of bytes.  A range that holds a whole segment writes its
-// output; pieces of a longer segment write partials that combine_kernel merges
-// in range order.
+// contiguous ranges, one per decode worker (a wave; the decode work-groups
+// hold 4 or 8 of them), so every wave streams the same number of bytes with
+// no synchronisation.  A range that holds a whole segment writes its output;
+// pieces of a longer segment write partials that combine_kernel merges in
+// range order.
 // ---------------------------------------------------------------------------
 
 // Launch-order tables of the sequences.  Decode entry e (a one-row sequence):
@@ -807,8 +808,8 @@ struct AttnArgs {
   int n_chunk_items;        // chunk work items (the first entries of the grid)
   int ch_target;            // work-group slots the chunk splits aim to fill
   int dec_units;            // stages in the decode stream
-  int dec_range;            // stages per decode work-group (the last may have fewer)
-  int dec_pmax;             // partial slots per decode work-group
+  int dec_range;            // stages per decode worker (the last may have fewer)
+  int dec_pmax;             // partial slots per decode worker
   int tabs_in_ws;           // tables in the workspace (1) or in `tabs` (0)
   float c;                  // sm_scale * log2(e)
   ArgTabs tabs;
@@ -861,21 +862,17 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
 }
 
 // One piece of a decode segment (row r0 of sequence s, KV head g, keys
-// [kb, ke), kb a multiple of 32): the NW waves of the work-group stream
-// consecutive ranges of 32-key stages, DEPTH stages ahead, with loads that
-// bypass the caches' retention (every byte is read once), then merge their
-// softmax states in LDS in wave order.  A whole segment writes the output, a
-// piece its partial at `slot`.
-template <int NB, int KF, int VF, int DEPTH, int NW>
-__device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int r0, int ctx, int g, int kb,
-                                    int ke, bool whole, int slot) {
-  using L = DecLayout<NB, KF, VF>;
+// [kb, ke), kb a multiple of 32), streamed by one wave: 32-key stages, DEPTH
+// stages ahead, with loads that bypass the caches' retention (every byte is
+// read once), through the wave's own LDS stage buffer wbuf.  A whole segment
+// writes the output, a piece its partial at `slot`.
+template <int NB, int KF, int VF, int DEPTH>
+__device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int r0, int ctx, int g, int kb,
+                                    int ke, bool whole, int64_t slot) {
   constexpr int D = 32 * NB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int nw = NW;
+  const int lane = threadIdx.x & 63;
   const int G = a.hq / a.hkv;
-  uint8_t* wbuf = smem + min(wave, nw - 1) * L::kWaveBytes;
-  const int n = lane & 15;
+  const int n = lane & 15, j = lane >> 4;
   ItemCtx ic;
   ic.k_pool = a.k_pool;
   ic.v_pool = a.v_pool;
@@ -883,14 +880,11 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
   ic.hkv = a.hkv;
   ic.g = g;
   ic.page_size = a.page_size;
-  const int per_wave = ceil_div(ceil_div(ke - kb, kStepKeys), nw) * kStepKeys;
-  const int kw0 = kb + wave * per_wave;
-  const int kw1 = wave < nw ? min(ke, kw0 + per_wave) : kw0;
-  const int nst = kw0 < kw1 ? ceil_div(kw1 - kw0, kStepKeys) : 0;
-  // page ids of the wave's 16-key runs, 64 at a time (one per lane)
+  const int nst = ceil_div(ke - kb, kStepKeys);
+  // page ids of the piece's 16-key runs, 64 at a time (one per lane)
   auto page_window = [&](int win) {
-    const int key = kw0 + 16 * (64 * win + lane);
-    return key < kw1 ? ic.bt_row[key / a.page_size] : 0;
+    const int key = kb + 16 * (64 * win + lane);
+    return key < ke ? ic.bt_row[key / a.page_size] : 0;
   };
   int my_page = page_window(0);
   Group<NB> gr;
@@ -906,16 +900,16 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
   auto issue = [&](DecWave<NB, KF, VF>& dw, int st) {
     const int run = 2 * st;
     const int p0 = page_of_run(run);
-    dw.load(ic, kw0 + st * kStepKeys, kw1, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
+    dw.load(ic, kb + st * kStepKeys, ke, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
   };
   auto consume = [&](DecWave<NB, KF, VF>& dw, int st) {
-    const int kbase = kw0 + st * kStepKeys;
+    const int kbase = kb + st * kStepKeys;
     dw.store(wbuf, lane);
     asm volatile("" ::: "memory");
-    dec_scales<NB, KF, VF>(wbuf, lane, a.c, kw1 - kbase);
+    dec_scales<NB, KF, VF>(wbuf, lane, a.c, ke - kbase);
     if (st + DEPTH < nst) issue(dw, st + DEPTH);
     asm volatile("" ::: "memory");
-    dec_compute<NB, KF, VF>(gr, wbuf, kbase, kw1, kbase + kStepKeys > kw1, lane);
+    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > ke, lane);
     asm volatile("" ::: "memory");
   };
 #pragma unroll
@@ -929,46 +923,31 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* smem, int s, int
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // every wave is done with its stage buffer
-  float* mo = reinterpret_cast<float*>(smem);  // [wave][16][D]
-  float* mm = mo + nw * 16 * D;                // [wave][16]
-  float* ml = mm + nw * 16;                    // [wave][16]
-  if (wave < nw) {
+  if (n >= G) return;
+  // lane (n, j) holds dims 16t + 4j + [0,4) of query head g*G + n
+  if (whole) {
+    float* dst = a.out + ((int64_t)r0 * a.hq + g * G + n) * D + 4 * j;
+    const float inv = 1.f / lsum;
 #pragma unroll
-    for (int tt = 0; tt < 2 * NB; ++tt)
+    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t] * inv;
+  } else {
+    const int64_t pi = slot * G + n;
+    float* dst = a.o_part + pi * D + 4 * j;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mo[(wave * 16 + n) * D + 16 * tt + 4 * (lane >> 4) + i] = gr.o[tt][i];
-    if (lane < 16) { mm[wave * 16 + n] = gr.m; ml[wave * 16 + n] = lsum; }
-  }
-  __syncthreads();
-  for (int u = tid; u < G * D; u += blockDim.x) {
-    const int hl = u / D, dd = u % D;
-    float M = -INFINITY;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, mm[w * 16 + hl]);
-    float Ls = 0.f, O = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float sc = __builtin_amdgcn_exp2f(mm[w * 16 + hl] - M);
-      Ls += ml[w * 16 + hl] * sc;
-      O += mo[(w * 16 + hl) * D + dd] * sc;
-    }
-    if (whole) {
-      a.out[((int64_t)r0 * a.hq + g * G + hl) * D + dd] = O / Ls;
-    } else {
-      const int64_t pi = (int64_t)slot * G + hl;
-      a.o_part[pi * D + dd] = O;
-      if (dd == 0) a.ml_part[pi] = make_float2(M, Ls);
-    }
+    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t];
+    if (j == 0) a.ml_part[pi] = make_float2(gr.m, lsum);
   }
 }
 
-// Decode work-group w: stages [w*R, min((w+1)*R, units)) of the decode stream,
-// one piece per segment it touches.  The work-group that runs a segment's
+// Decode worker w (one wave): stages [w*R, min((w+1)*R, units)) of the decode
+// stream, one piece per segment it touches.  The worker that runs a segment's
 // first stage records where the segment's results went.
-template <int NB, int KF, int VF, int DEPTH, int NW>
-__device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
+template <int NB, int KF, int VF, int DEPTH>
+__device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
+  const int x0 = w * a.dec_range, x1 = min(x0 + a.dec_range, a.dec_units);
+  if (x0 >= x1) return;
   const TabView tv = tab_view(a);
   const int G = a.hq / a.hkv;
-  const int x0 = w * a.dec_range, x1 = min(x0 + a.dec_range, a.dec_units);
   int e = wave_find(tv.dec_unit, a.n_dec, x0);
   int x = x0, k = 0;
   while (x < x1) {
@@ -979,12 +958,12 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
     const int p_hi = min(x1, seg_hi);
     const int r0 = tv.dec_r0[e];
     const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
-    const int slot = w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF, DEPTH, NW>(a, smem, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
-                             min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
-    if (first && threadIdx.x == 0) {
+    const int64_t slot = (int64_t)w * a.dec_pmax + k;
+    decode_piece<NB, KF, VF, DEPTH>(a, wbuf, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
+                                    min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
+    if (first && (threadIdx.x & 63) == 0) {
       DirEntry d;
-      d.slot = slot;
+      d.slot = (int)slot;
       d.wg = w;
       d.n = whole ? 1 : (seg_hi - 1) / a.dec_range - w + 1;
       d.rh0 = r0 * a.hq + g * G;
@@ -993,7 +972,6 @@ __device__ inline void decode_wg(const AttnArgs& a, uint8_t* smem, int w) {
     x = p_hi;
     ++k;
     if (x == seg_hi && g + 1 == a.hkv) ++e;
-    __syncthreads();  // the LDS of this piece is free again
   }
 }
 
@@ -1228,14 +1206,14 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
       return;
     }
   }
-  decode_wg<NB, KF, VF, 2, HAS_CHUNK ? kMixedWaves : kDecodeWaves>(a, smem, b - a.n_chunk_items);
+  constexpr int nw = HAS_CHUNK ? kMixedWaves : kDecodeWaves;
+  const int wave = threadIdx.x >> 6;
+  decode_worker<NB, KF, VF, 2>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes, (b - a.n_chunk_items) * nw + wave);
 }
 
 template <int NB, int KF, int VF>
 constexpr int decode_smem_bytes(int waves) {
-  const int stages = waves * DecLayout<NB, KF, VF>::kWaveBytes;
-  const int merge = (waves * 16 * 32 * NB + 2 * waves * 16) * 4;
-  return stages > merge ? stages : merge;
+  return waves * DecLayout<NB, KF, VF>::kWaveBytes;  // one stage buffer per wave
 }
 
 template <int NB, int KF, int VF>
@@ -1264,14 +1242,15 @@ decode_attention_kernel(AttnArgs a) {
   attention_body<NB, KF, VF, false>(a, smem);
 }
 
-// Merges the pieces of decode segments that span several decode work-groups.
+// Merges the pieces of decode segments that span several decode workers.
 // One work-group per (segment, query head of the group, 32 dims): thread
-// (phase ph, dim) folds pieces ph, ph+8, ph+16, ... into a running (m, l, o)
-// with eight independent loads in flight, then the eight phases are folded in
-// phase order.  The order depends only on the piece count: deterministic.
-constexpr int kCombinePhases = 8;
-constexpr int kCombineThreads = 32 * kCombinePhases;
-constexpr int kCombineUnroll = 8;
+// (phase ph, dim) folds pieces ph, ph+P, ph+2P, ... into a running (m, l, o)
+// with up to sixteen loads in flight, then the P phases are folded pairwise in
+// a fixed tree.  P = 8, or 32 when some segment has more than
+// kCombineWidePieces pieces.  The order depends only on the piece count and
+// P: deterministic.
+constexpr int kCombineUnroll = 16;
+constexpr int kCombineWidePieces = 128;
 
 __device__ inline void lse_fold(float& m, float& l, float& o, float m2, float l2, float o2) {
   const float mn = fmaxf(m, m2);
@@ -1282,9 +1261,11 @@ __device__ inline void lse_fold(float& m, float& l, float& o, float m2, float l2
   m = mn;
 }
 
-__global__ void __launch_bounds__(kCombineThreads)
+template <int P>
+__global__ void __launch_bounds__(32 * P)
 combine_kernel(AttnArgs a, int head_dim) {
-  __shared__ float red[3][kCombineThreads];
+  constexpr int kCombinePhases = P;
+  __shared__ float red[3][32 * P];
   const int G = a.hq / a.hkv, ndg = head_dim / 32;
   const int seg = blockIdx.x / (G * ndg), rem = blockIdx.x % (G * ndg);
   const int hl = rem / ndg, dd = (rem % ndg) * 32 + (threadIdx.x & 31);
@@ -1310,17 +1291,19 @@ combine_kernel(AttnArgs a, int head_dim) {
 #pragma unroll
     for (int u = 0; u < kCombineUnroll; ++u) lse_fold(m, l, o, ml[u].x, ml[u].y, ov[u]);
   }
-  red[0][threadIdx.x] = m;
-  red[1][threadIdx.x] = l;
-  red[2][threadIdx.x] = o;
-  __syncthreads();
-  if (ph == 0) {
-    for (int k = 1; k < kCombinePhases; ++k) {
-      const int t = 32 * k + (threadIdx.x & 31);
+  // fixed pairwise tree over the phases: phase ph takes phase ph + half
+  for (int half = kCombinePhases / 2; half >= 1; half >>= 1) {
+    red[0][threadIdx.x] = m;
+    red[1][threadIdx.x] = l;
+    red[2][threadIdx.x] = o;
+    __syncthreads();
+    if (ph < half) {
+      const int t = threadIdx.x + 32 * half;
       lse_fold(m, l, o, red[0][t], red[1][t], red[2][t]);
     }
-    a.out[((int64_t)d.rh0 + hl) * head_dim + dd] = o / l;
+    __syncthreads();
   }
+  if (ph == 0) a.out[((int64_t)d.rh0 + hl) * head_dim + dd] = o / l;
 }
 
 // Merges the key splits of chunk tiles cut into more than one split.  A tile
@@ -1460,6 +1443,7 @@ struct HostPlan {
   int n_dec = 0, n_chunk = 0, n_chunk_items = 0, ch_target = 1;
   bool ch_splits = false;  // some chunk tile is cut into several splits
   int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
+  int dec_seg_pieces = 1;  // pieces of the most cut decode segment
   int64_t n_slots = 0;
 };
 
@@ -1508,30 +1492,31 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->ch_splits = ch_splits;
   hp->dec_units = (int)units;
   if (units > 0) {
-    // equal ranges, as many as fit on the device at once (fewer for small
-    // batches: at least kMinWaveStages stages per wave each); decode-only
-    // batches run two 4-wave work-groups per compute unit, mixed ones one
-    // 8-wave work-group
-    const bool mixed = n_chunk > 0;
-    const int64_t max_wgs = (int64_t)(mixed ? 1 : 2) * cus;
-    const int64_t min_stages = (int64_t)kMinWaveStages * (mixed ? kMixedWaves : kDecodeWaves);
-    int64_t wgs = std::min<int64_t>(max_wgs, std::max<int64_t>(1, units / min_stages));
-    const int64_t range = ceil_div64(units, wgs);
-    wgs = ceil_div64(units, range);
-    hp->dec_wgs = (int)wgs;
+    // equal ranges, one per decode worker (a wave), as many as the device
+    // holds at once (eight waves per compute unit: two 4-wave work-groups of
+    // the decode kernel or one 8-wave work-group of the mixed kernel), fewer
+    // for small batches: at least kMinWaveStages stages each
+    const int nw = n_chunk > 0 ? kMixedWaves : kDecodeWaves;
+    const int64_t max_workers = (int64_t)8 * cus;
+    int64_t workers = std::min<int64_t>(max_workers, std::max<int64_t>(1, units / kMinWaveStages));
+    const int64_t range = ceil_div64(units, workers);
+    workers = ceil_div64(units, range);
+    hp->dec_wgs = (int)ceil_div64(workers, nw);
     hp->dec_range = (int)range;
-    // pieces per work-group: one plus the segment starts strictly inside its range
-    std::vector<int> pieces((size_t)wgs, 1);
+    // pieces per worker: one plus the segment starts strictly inside its range
+    std::vector<int> pieces((size_t)workers, 1);
     int64_t x = 0;
     for (int s = 0; s < B->num_seqs; ++s) {
       const int q_len = B->q_start_host[s + 1] - B->q_start_host[s];
       if (q_len > 1) continue;
       const int nst = dec_stages(B->prefix_len_host[s] + 1);
-      for (int g = 0; g < hkv; ++g, x += nst)
+      for (int g = 0; g < hkv; ++g, x += nst) {
         if (x % range != 0) ++pieces[(size_t)(x / range)];
+        hp->dec_seg_pieces = std::max<int>(hp->dec_seg_pieces, (int)((x + nst - 1) / range - x / range + 1));
+      }
     }
     hp->dec_pmax = *std::max_element(pieces.begin(), pieces.end());
-    hp->n_slots = (int64_t)wgs * hp->dec_pmax;
+    hp->n_slots = (int64_t)workers * hp->dec_pmax;
   }
   return MAB_OK;
 }
@@ -1708,8 +1693,11 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   }
   if (hp.n_dec > 0) {
     const int G = layout->num_q_heads / layout->num_kv_heads;
-    hipLaunchKernelGGL(combine_kernel, dim3(hp.n_dec * layout->num_kv_heads * G * (layout->head_dim / 32)),
-                       dim3(kCombineThreads), 0, hs, a, layout->head_dim);
+    const dim3 cgrid(hp.n_dec * layout->num_kv_heads * G * (layout->head_dim / 32));
+    if (hp.dec_seg_pieces > kCombineWidePieces)
+      hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(32 * 32), 0, hs, a, layout->head_dim);
+    else
+      hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(32 * 8), 0, hs, a, layout->head_dim);
   }
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }

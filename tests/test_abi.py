@@ -62,15 +62,14 @@ def _ws(layout, batch):
     return mab._lib().attention_workspace_bytes(ctypes.byref(layout), ctypes.byref(batch.struct))
 
 
-def _decode_plan(ctxs, hkv, cus=256, per_cu=2, min_stages=16):
+def _decode_plan(ctxs, hkv, cus=256):
     """The decode stream's cut, restated from its rule: the segments (one per
     decode row and KV head, ceil(ctx/32) stages each) laid end to end, cut into
-    equal ranges, at most per_cu per compute unit and at least min_stages
-    stages each (4 per wave: decode-only batches run two 4-wave work-groups
-    per compute unit, batches with a chunk one 8-wave work-group); pieces per
-    range = 1 + segment starts strictly inside it."""
+    equal ranges, one per worker (a wave), at most 8 per compute unit and at
+    least 4 stages each; pieces per range = 1 + segment starts strictly inside
+    it.  Returns (workers, range, pieces per worker at most)."""
     units = sum(hkv * -(-c // 32) for c in ctxs)
-    wgs = min(per_cu * cus, max(1, units // min_stages))
+    wgs = min(8 * cus, max(1, units // 4))
     rng = -(-units // wgs)
     wgs = -(-units // rng)
     pieces = [1] * wgs
@@ -103,8 +102,8 @@ def test_workspace_closed_form():
     lay = mab.make_layout(24, 4, 128, 256, 1000)
     b = _HostBatch([0, 1, 2, 50], [1000, 70000, 300], max_pages=400)  # 2 decode rows + 48-row chunk
     n = _ws(lay, b)
-    wgs, rng, pmax = _decode_plan([1001, 70001], 4, per_cu=1, min_stages=32)  # a batch with a chunk
-    assert (wgs, rng, pmax) == (254, 35, 2)
+    wgs, rng, pmax = _decode_plan([1001, 70001], 4)
+    assert (wgs, rng, pmax) == (1776, 5, 2)
     tiles, f, h, rows = _chunk_plan(48, 4, 6)
     assert (tiles, f, h, rows) == (12, 8, 2, 128)
     slots = wgs * pmax
