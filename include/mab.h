@@ -117,7 +117,9 @@ int32_t kv_block_bytes(int32_t format);
 int64_t kv_pool_bytes(const mab_kv_layout* layout, int32_t format);
 
 /* Device workspace that mixed_attention_fwd needs for this batch (split-K
- * partial results and small per-row tables).  Computed from the host mirrors.
+ * partial results and small per-row tables).  Computed from the host mirrors
+ * and the current device's compute-unit count (the work is cut to fill that
+ * device), so query it on the device the call will run on.
  * Returns a negative status (-MAB_ERR_*) if the layout or batch is invalid. */
 int64_t attention_workspace_bytes(const mab_kv_layout* layout, const mab_batch* batch);
 
@@ -150,12 +152,16 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch,
  * where K_hat, V_hat are the dequantized cache blocks.  Arithmetic: fp16
  * operands on the matrix cores with fp32 accumulation, fp32 online softmax,
  * split-K over key ranges merged by log-sum-exp in fixed order.  The result
- * is deterministic and independent of the physical page ids and of which
- * other sequences share the batch.
+ * is deterministic (bit-identical run to run) and independent of the
+ * physical page ids.  Rows of a chunk sequence (q_len > 1) are also
+ * bit-identical whatever else shares the batch; a decode row's key range is
+ * cut according to the whole batch, so it may differ in the last bits
+ * (within 1e-3 at unit-scale values) between different batches.
  *
  * q          : device fp16 [num_rows][Hq][D], read only.
  * k_pool, v_pool : device pools, read only.
- * sm_scale   : softmax scale (typically 1/sqrt(D)).
+ * sm_scale   : softmax scale (typically 1/sqrt(D)); must be positive and
+ *              finite (MAB_ERR_UNSUPPORTED otherwise).
  * out        : device fp32 [num_rows][Hq][D], fully written.
  * workspace  : device scratch of at least attention_workspace_bytes() bytes,
  *              owned by the caller; contents need not be initialized and are

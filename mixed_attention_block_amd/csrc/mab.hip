@@ -36,7 +36,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte 
 constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two work-groups per CU)
 constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
 constexpr int kStepKeys = 32;       // keys per stage / tile
-constexpr int kChunkSplit = 1 << 30;  // keys per chunk split (no split: a tile sees all its keys)
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr int kMaxSeqs = 4096;
 constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this many stages per wave
@@ -242,12 +241,6 @@ __device__ inline half8_t nibble_order(half8_t q) {
   return half8_t{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
 }
 
-// Max / sum over the two 32-lane halves (lanes l and l^32).  (The gfx950
-// lane-swap builtin was miscompiled here: its second result was dropped.)
-__device__ inline float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-
-__device__ inline float sum_halves(float x) { return x + __shfl_xor(x, 32); }
-
 // Max over lanes l and l^16 (l^32): the row-swap instructions put the values
 // of both lanes of a pair into the two results, in either order.
 __device__ inline float max_xor16(float x) {
@@ -283,17 +276,6 @@ struct DecLayout {
   static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
   static_assert(kKBytes % 16 == 0 && kVBytes % 16 == 0 && kWaveBytes % 16 == 0, "alignment");
 };
-
-// Address of 16-byte chunk ch of the stage whose runs start at k0/k1 (K) and
-// v0/v1 (V); chunks past the end re-read the last one.
-template <int NB, int KF, int VF>
-__device__ inline const uint8_t* stage_chunk(int ch, const uint8_t* k0, const uint8_t* k1, const uint8_t* v0,
-                                             const uint8_t* v1) {
-  using L = DecLayout<NB, KF, VF>;
-  if (ch < L::kChunksK) return ch < L::kRecK ? k0 + 16 * ch : k1 + 16 * (ch - L::kRecK);
-  const int cv = min(ch - L::kChunksK, L::kChunksV - 1);
-  return cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
-}
 
 __device__ inline uint32_t lds_u32(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
