@@ -217,10 +217,18 @@ struct ItemCtx {
 template <int NB>
 struct Group {
   half8_t q[NB];          // Q^T operand: slot l%16, dims 32b + 8(l/16) + [0,8)
-  float4_t o[2 * NB];     // O^T: slot l%16, dims 16t + 4(l/16) + [0,4)
+  float4_t o[2 * NB];     // O^T: slot l%16, dims 16t + 4(l/16) + [0,4), V codes taken with their bias
+  float4_t vb[NB];        // per block: sum over keys of the P * V-scale weights (the bias correction of o)
   float m, l;             // running max (log2 units) and lane-partial sum
   int limit;              // last key position visible to the slot (-1: none)
 };
+
+// V codes enter the PV products as fp16 integers carrying the bias of the
+// magic-number conversion (1152 + code for 8-bit codes, 1032 + code for
+// 4-bit codes); o is corrected once at the end by bias * (sum of weights).
+template <int F> struct VBias;
+template <> struct VBias<MAB_KV_Q8> { static constexpr float kBias = 1152.f; };
+template <> struct VBias<MAB_KV_Q4> { static constexpr float kBias = 1032.f; };
 
 template <int NB>
 __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
@@ -231,6 +239,8 @@ __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, 
   }
 #pragma unroll
   for (int t = 0; t < 2 * NB; ++t) gr.o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < NB; ++b) gr.vb[b] = float4_t{0.f, 0.f, 0.f, 0.f};
   gr.m = -INFINITY;
   gr.l = 0.f;
   gr.limit = qrow ? limit : -1;
@@ -327,18 +337,17 @@ __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
 }
 
 // Codes of value index dv (within block) for two keys at byte offsets o0, o1 of
-// their block payloads, as an fp16 pair of exact integers.
+// their block payloads, as an fp16 pair of exact integers offset by
+// VBias<F>::kBias (1152 + code, or 1032 + code for 4-bit codes).
 template <int F>
-__device__ inline half2_t lds_code_pair(const uint8_t* base, int o0, int o1, int dv) {
+__device__ inline half2_t lds_code_pair_biased(const uint8_t* base, int o0, int o1, int dv) {
   if constexpr (F == MAB_KV_Q8) {
     const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
-    const half2_t bias = {(half_t)-1152.f, (half_t)-1152.f};
-    return __builtin_bit_cast(half2_t, w ^ 0x64806480u) + bias;
+    return __builtin_bit_cast(half2_t, w ^ 0x64806480u);
   } else {
     uint32_t w = (uint32_t)base[o0 + (dv >> 1)] | ((uint32_t)base[o1 + (dv >> 1)] << 16);
     w = ((dv & 1) ? (w >> 4) : w) & 0x000F000Fu;
-    const half2_t bias = {(half_t)-1032.f, (half_t)-1032.f};
-    return __builtin_bit_cast(half2_t, w ^ 0x64086408u) + bias;
+    return __builtin_bit_cast(half2_t, w ^ 0x64086408u);
   }
 }
 
@@ -414,7 +423,9 @@ __device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
 // fp32 block scales, online softmax with a stale max (rescaled only when the
 // running max grows by more than 2^kRescaleSlack), then O^T += V^T (P * V
 // scale) with P rounded to fp16 once and multiplied by the fp16 V scale of
-// each block.  `tail`: the stage holds keys at or past kend (masked).
+// each block.  The V codes enter with the bias of their conversion; the sum
+// of each block's weights (an MFMA against ones) removes it at the end.
+// `tail`: the stage holds keys at or past kend (masked).
 template <int NB, int KF, int VF>
 __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, int lane) {
   using L = DecLayout<NB, KF, VF>;
@@ -452,6 +463,8 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     const float alpha = grow ? __builtin_amdgcn_exp2f(gr.m - m_new) : 1.f;  // 0 when m was -inf
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) gr.vb[b] *= alpha;
     gr.l *= alpha;
     gr.m = m_new;
   }
@@ -474,6 +487,8 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     const half4_t s0 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 4 * j);
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
     const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int dv = 16 * t2 + n;  // value index inside block b
@@ -481,8 +496,8 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
-        vp[e] = lds_code_pair<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + 2,
-                                  (ka + 1) * L::kRecV + b * L::kBV + 2, dv);
+        vp[e] = lds_code_pair_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + 2,
+                                         (ka + 1) * L::kRecV + b * L::kBV + 2, dv);
       }
       const half8_t vc = half8_t{vp[0][0], vp[0][1], vp[1][0], vp[1][1], vp[2][0], vp[2][1], vp[3][0], vp[3][1]};
       gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
@@ -646,22 +661,31 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
   // the QK products at a raised issue priority: the matrix cores get fed while
   // the other wave of the SIMD is in its softmax or dequantization
   __builtin_amdgcn_s_setprio(2);
+  // every product first (16 independent MFMAs), then the block scales: the
+  // scale FMAs never wait on an MFMA issued just before them
+  float4_t pb[2][NB][2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    s[kt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-    s[kt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
     const half_t* kr = t.k + (16 * kt + n) * T::kStride + 8 * j;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const half8_t ka = *reinterpret_cast<const half8_t*>(kr + 32 * b);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        pb[kt][b][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, cw.q[rt][b], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+    s[kt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
       const half4_t kd = *reinterpret_cast<const half4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, cw.q[rt][b], float4_t{0.f, 0.f, 0.f, 0.f},
-                                                                   0, 0, 0);
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kt][rt][i] = __builtin_fmaf((float)kd[i], pb[i], s[kt][rt][i]);
-      }
+        for (int i = 0; i < 4; ++i) s[kt][rt][i] = __builtin_fmaf((float)kd[i], pb[kt][b][rt][i], s[kt][rt][i]);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -906,6 +930,11 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (n >= G) return;
+  // remove the code bias: o -= bias * (sum of the block's weights)
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
   // lane (n, j) holds dims 16t + 4j + [0,4) of query head g*G + n
   if (whole) {
     float* dst = a.out + ((int64_t)r0 * a.hq + g * G + n) * D + 4 * j;
