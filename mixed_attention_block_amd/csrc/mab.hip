@@ -33,6 +33,17 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
+// Loads through global-address-space pointers.  Every buffer the kernels
+// read is device global memory; saying so makes the compiler emit global
+// loads, which count only against the vector-memory counter (a generic
+// pointer gives flat loads, which also count against the LDS counter, so that
+// every wait for an LDS result would also wait for the loads in flight).
+#define MAB_GLOBAL __attribute__((address_space(1)))
+__device__ inline u32x4_t gload16_nt(const void* p) {
+  return __builtin_nontemporal_load((const MAB_GLOBAL u32x4_t*)p);
+}
+__device__ inline int32_t gload_i32(const int32_t* p) { return *(const MAB_GLOBAL int32_t*)p; }
+
 constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two work-groups per CU)
 constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
 constexpr int kStepKeys = 32;       // keys per stage / tile
@@ -351,10 +362,47 @@ __device__ inline half2_t lds_code_pair_biased(const uint8_t* base, int o0, int 
   }
 }
 
+// p, which holds the same value in every lane, as a value the compiler keeps
+// in scalar registers.
+template <typename T>
+__device__ inline const T* wave_uniform(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int NB, int KF, int VF>
 struct DecWave {
   using L = DecLayout<NB, KF, VF>;
   u32x4_t r[L::kLoads];  // the next stage's raw bytes, in flight
+
+  // The loads of a stage whose 32 keys lie in one page (page_size a multiple
+  // of 32): its K bytes and its V bytes are each one contiguous run, so every
+  // load is a scalar run base plus a lane offset that does not change from
+  // stage to stage (16*lane + 1024*i, clamped on the last load); only the
+  // load that straddles the K/V boundary picks its base per lane.
+  __device__ __attribute__((always_inline)) void load_page(const ItemCtx& c, int kbase, int page, int lane) {
+    const int64_t tok = ((int64_t)page * c.hkv + c.g) * c.page_size + kbase % c.page_size;
+    const uint8_t* kr = wave_uniform(c.k_pool + tok * L::kRecK);
+    const uint8_t* vr = wave_uniform(c.v_pool + tok * L::kRecV);
+    const uint32_t lo = 16u * (uint32_t)lane;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < L::kLoads; ++i) {
+      const uint8_t* src;
+      if (64 * i + 63 < L::kChunksK) {
+        src = kr + (lo + 1024u * i);
+      } else if (64 * i >= L::kChunksK) {
+        const int c0 = 64 * i - L::kChunksK;
+        if (64 * i + 63 < L::kChunks) src = vr + (lo + 16u * c0);
+        else src = vr + 16u * (uint32_t)min(lane + c0, L::kChunksV - 1);  // lanes past the last chunk re-read it
+      } else {
+        const int ch = lane + 64 * i;
+        src = ch < L::kChunksK ? kr + 16u * (uint32_t)ch : vr + 16u * (uint32_t)(ch - L::kChunksK);
+      }
+      r[i] = gload16_nt(src);  // streamed once
+    }
+  }
 
   // Issue the loads of keys [kbase, kbase+32) of KV head c.g: two 16-key runs,
   // each inside one page (ids page0, page1).  A run at or past kend re-reads
@@ -384,7 +432,7 @@ struct DecWave {
             : ch < L::kChunksK ? k1 + 16 * (ch - L::kRecK)
             : cv < L::kRecV ? v0 + 16 * cv : v1 + 16 * (cv - L::kRecV);
       }
-      r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));  // streamed once
+      r[i] = gload16_nt(src);  // streamed once
     }
   }
 
@@ -455,8 +503,7 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
   }
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx));
   const bool grow = mx > gr.m + kRescaleSlack;  // also true for the first keys (m = -inf)
   if (__any(grow)) {
     const float m_new = grow ? mx : gr.m;
@@ -525,14 +572,9 @@ struct ChunkTile {
   half_t kd[NB * kStepKeys];               // K block scale (exact), [block][key]
 };
 
-// Position of value index e (0..31) of a block inside its LDS row segment.
-// 4-bit codes are unpacked low nibbles first, so each group of 8 values is
-// stored in the order (0,2,4,6,1,3,5,7); Q and the output follow suit.
-template <int F>
-__device__ inline int slot_of_value(int e) {
-  if constexpr (F == MAB_KV_Q8) return e;
-  else return (e & ~7) | ((e & 1) << 2) | ((e & 7) >> 1);
-}
+// Value index (0..31 within a block) held at position p of a block's LDS row
+// segment.  4-bit codes are unpacked low nibbles first, so each group of 8
+// values is stored in the order (0,2,4,6,1,3,5,7); Q and the output follow suit.
 template <int F>
 __device__ inline int value_of_slot(int p) {
   if constexpr (F == MAB_KV_Q8) return p;
@@ -603,8 +645,6 @@ __device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, boo
     t.kd[b * kStepKeys + key] = d;
   }
 }
-
-typedef _Float16 half4v_t __attribute__((ext_vector_type(4)));
 
 __device__ inline half4_t lds_tr16(const half_t* p) {
   typedef short s4_t __attribute__((ext_vector_type(4)));
@@ -890,7 +930,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   // page ids of the piece's 16-key runs, 64 at a time (one per lane)
   auto page_window = [&](int win) {
     const int key = kb + 16 * (64 * win + lane);
-    return key < ke ? ic.bt_row[key / a.page_size] : 0;
+    return key < ke ? gload_i32(ic.bt_row + key / a.page_size) : 0;
   };
   int my_page = page_window(0);
   Group<NB> gr;
@@ -903,10 +943,12 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
     if (run > 0 && (run & 63) == 0) my_page = page_window(run >> 6);
     return __builtin_amdgcn_readlane(my_page, run & 63);
   };
+  const bool one_page = a.page_size % kStepKeys == 0;  // every stage inside one page (kb % 32 == 0)
   auto issue = [&](DecWave<NB, KF, VF>& dw, int st) {
     const int run = 2 * st;
     const int p0 = page_of_run(run);
-    dw.load(ic, kb + st * kStepKeys, ke, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
+    if (one_page) dw.load_page(ic, kb + st * kStepKeys, p0, lane);
+    else dw.load(ic, kb + st * kStepKeys, ke, p0, __builtin_amdgcn_readlane(my_page, (run + 1) & 63), lane);
   };
   auto consume = [&](DecWave<NB, KF, VF>& dw, int st) {
     const int kbase = kb + st * kStepKeys;
@@ -984,16 +1026,6 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
     ++k;
     if (x == seg_hi && g + 1 == a.hkv) ++e;
   }
-}
-
-// p, which holds the same value in every lane, as a value the compiler keeps
-// in scalar registers.
-template <typename T>
-__device__ inline const T* wave_uniform(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
 // Chunk work item: row tile qt (R rows) of a chunk sequence, KV head g, head
