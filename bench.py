@@ -38,13 +38,15 @@ WORKLOADS = {
                 "page 256, contexts uniform in [1024, 32768], 2% K outlier channels x20, 1 layer",
     "mixed16_chunk2k": "16 decode rows (contexts uniform in [2048, 65536]) + one 2048-row chunk at "
                        "position 131072, 24/4 heads, head_dim 128, q8, page 256, K outliers, 1 layer",
+    "decode16_f16": "the decode16 batch (16 decode rows, contexts uniform in [1024, 32768], 24/4 heads, "
+                    "head_dim 128, page 256) over an unquantized f16 cache (64-byte blocks), 1 layer",
     "long_q8": "one decode row at context 262144, 24/4 heads, head_dim 128, q8, page 256, 1 layer",
     "long_k4v4": "one decode row at context 262144, 24/4 heads, head_dim 128, K4V4 18-byte blocks, "
                  "page 256, 1 layer",
     "step_k4v4": "12 attention layers, each: 16 decode rows (contexts log-uniform in [512, 262144]) + "
                  "a 2048-row chunk at 131072, 24/4 heads, head_dim 128, K4V4, page 256, K outliers",
 }
-SEEDS = {"decode16": 2, "mixed16_chunk2k": 3, "long_q8": 4, "long_k4v4": 4, "step_k4v4": 5}
+SEEDS = {"decode16": 2, "decode16_f16": 2, "mixed16_chunk2k": 3, "long_q8": 4, "long_k4v4": 4, "step_k4v4": 5}
 
 
 def kv_bytes_per_position(layout):

@@ -33,6 +33,8 @@
  *             q8 (34 B): 32 two's-complement int8 codes.
  *             q4 (18 B): 16 bytes, byte j = code 2j (low nibble) | code 2j+1
  *                        (high nibble), two's-complement nibbles.
+ *             f16 (64 B): the unquantized mode of the same table: the 32
+ *                        values as little-endian IEEE halves, no scale.
  *             value = code * d.  Encoding: s = fl32(max|x| / Q) (Q = 127 or 7,
  *             IEEE binary32 divide), code = clamp(rint_even(fl32(x / s)), -Q, Q),
  *             d = fp16 round-to-nearest-even of s (no flush); all-zero block:
@@ -54,7 +56,8 @@
  * Supported shapes (others return MAB_ERR_UNSUPPORTED or MAB_ERR_SHAPE):
  *   head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with a group of at
  *   most 8 query heads per KV head; page_size a positive multiple of 16;
- *   1 <= rows per sequence; num_seqs <= 4096; all buffers 16-byte aligned.
+ *   1 <= rows per sequence; num_seqs <= 4096; all buffers 16-byte aligned;
+ *   k_format and v_format both MAB_KV_F16 or neither.
  */
 #ifndef MAB_H
 #define MAB_H
@@ -77,10 +80,11 @@ enum {
   MAB_ERR_HIP = 6          /* the HIP runtime refused a kernel launch          */
 };
 
-/* KV block formats (MBufo page, section 2 modes table). */
+/* KV block formats (MBufo page, section 2 modes table and occupancy table). */
 enum {
-  MAB_KV_Q8 = 1, /* 34-byte block: fp16 scale + 32 x int8            */
-  MAB_KV_Q4 = 2  /* 18-byte block: fp16 scale + 16 bytes of 32 x int4 */
+  MAB_KV_Q8 = 1,  /* 34-byte block: fp16 scale + 32 x int8            */
+  MAB_KV_Q4 = 2,  /* 18-byte block: fp16 scale + 16 bytes of 32 x int4 */
+  MAB_KV_F16 = 3  /* 64-byte block: 32 x fp16, unquantized (K and V both f16 only) */
 };
 
 /* Shape of the cache and of the attention heads. */
@@ -90,8 +94,8 @@ typedef struct mab_kv_layout {
   int32_t head_dim;     /* D                                     */
   int32_t page_size;    /* tokens per page                       */
   int32_t num_pages;    /* pages in each pool                    */
-  int32_t k_format;     /* MAB_KV_Q8 or MAB_KV_Q4                */
-  int32_t v_format;     /* MAB_KV_Q8 or MAB_KV_Q4                */
+  int32_t k_format;     /* MAB_KV_Q8, MAB_KV_Q4 or MAB_KV_F16    */
+  int32_t v_format;     /* same; f16 only together with f16      */
   int32_t reserved;     /* must be 0                             */
 } mab_kv_layout;
 
@@ -108,7 +112,7 @@ typedef struct mab_batch {
   const int32_t* prefix_len_host; /* host mirror of prefix_len                    */
 } mab_batch;
 
-/* Bytes of one 32-value block of `format` (34 or 18); 0 for an unknown format. */
+/* Bytes of one 32-value block of `format` (34, 18 or 64); 0 for an unknown format. */
 int32_t kv_block_bytes(int32_t format);
 
 /* Bytes of one pool of `format` for `layout`:

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libmab.so")
 
 MAB_KV_Q8 = 1
 MAB_KV_Q4 = 2
-FORMATS = {"q8": MAB_KV_Q8, "q4": MAB_KV_Q4}
+MAB_KV_F16 = 3
+FORMATS = {"q8": MAB_KV_Q8, "q4": MAB_KV_Q4, "f16": MAB_KV_F16}
 
 
 class MabError(RuntimeError):
@@ -71,7 +72,7 @@ def _lib():
 
 def make_layout(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, k_format="q8",
                 v_format="q8"):
-    """A ``KVLayout``; formats are "q8"/"q4" or the MAB_KV_* integers."""
+    """A ``KVLayout``; formats are "q8"/"q4"/"f16" or the MAB_KV_* integers."""
     kf = FORMATS.get(k_format, k_format)
     vf = FORMATS.get(v_format, v_format)
     return KVLayout(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kf, vf, 0)

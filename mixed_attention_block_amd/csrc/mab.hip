@@ -56,6 +56,10 @@ constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is
 template <int F> struct Fmt;
 template <> struct Fmt<MAB_KV_Q8> { static constexpr int kBytes = 34; static constexpr int kQmax = 127; };
 template <> struct Fmt<MAB_KV_Q4> { static constexpr int kBytes = 18; static constexpr int kQmax = 7; };
+// the unquantized mode: a block is its 32 values as fp16, no scale
+template <> struct Fmt<MAB_KV_F16> { static constexpr int kBytes = 64; static constexpr int kQmax = 0; };
+// offset of a block's values (after the scale of the quantized formats)
+template <int F> constexpr int kPayload = F == MAB_KV_F16 ? 0 : 2;
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -142,45 +146,51 @@ __device__ inline int find_seq(const int32_t* __restrict__ q_start, int num_seqs
 
 template <int F>
 __device__ inline void encode_block(const half_t* __restrict__ x, uint8_t* __restrict__ dst) {
-  constexpr int Q = Fmt<F>::kQmax;
-  float xf[32];
+  if constexpr (F == MAB_KV_F16) {  // the values themselves (blocks of 64 bytes, 16-byte aligned)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half8_t v = *reinterpret_cast<const half8_t*>(x + 8 * i);
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<half8_t*>(dst)[i] = reinterpret_cast<const half8_t*>(x)[i];
+  } else {
+    constexpr int Q = Fmt<F>::kQmax;
+    float xf[32];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xf[8 * i + e] = (float)v[e];
-  }
-  float amax = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const half8_t v = *reinterpret_cast<const half8_t*>(x + 8 * i);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xf[i]));
-  int code[32];
-  uint16_t dbits = 0;
-  if (amax > 0.f) {
-    const float s = amax / (float)Q;                 // IEEE binary32 divide
-    const half_t d = (half_t)s;                      // RNE, fp16 subnormals kept
-    dbits = __builtin_bit_cast(uint16_t, d);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float r = rintf(xf[i] / s);                    // half to even
-      r = fminf(fmaxf(r, -(float)Q), (float)Q);
-      code[i] = (int)r;
+      for (int e = 0; e < 8; ++e) xf[8 * i + e] = (float)v[e];
     }
-  } else {
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) code[i] = 0;
-  }
-  uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);  // blocks start on even bytes
-  d16[0] = dbits;
-  if constexpr (F == MAB_KV_Q8) {
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xf[i]));
+    int code[32];
+    uint16_t dbits = 0;
+    if (amax > 0.f) {
+      const float s = amax / (float)Q;                 // IEEE binary32 divide
+      const half_t d = (half_t)s;                      // RNE, fp16 subnormals kept
+      dbits = __builtin_bit_cast(uint16_t, d);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      d16[1 + i] = (uint16_t)((code[2 * i] & 0xFF) | ((code[2 * i + 1] & 0xFF) << 8));
-  } else {
+      for (int i = 0; i < 32; ++i) {
+        float r = rintf(xf[i] / s);                    // half to even
+        r = fminf(fmaxf(r, -(float)Q), (float)Q);
+        code[i] = (int)r;
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int b0 = (code[4 * i] & 0xF) | ((code[4 * i + 1] & 0xF) << 4);
-      const int b1 = (code[4 * i + 2] & 0xF) | ((code[4 * i + 3] & 0xF) << 4);
-      d16[1 + i] = (uint16_t)(b0 | (b1 << 8));
+      for (int i = 0; i < 32; ++i) code[i] = 0;
+    }
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);  // blocks start on even bytes
+    d16[0] = dbits;
+    if constexpr (F == MAB_KV_Q8) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        d16[1 + i] = (uint16_t)((code[2 * i] & 0xFF) | ((code[2 * i + 1] & 0xFF) << 8));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int b0 = (code[4 * i] & 0xF) | ((code[4 * i + 1] & 0xF) << 4);
+        const int b1 = (code[4 * i + 2] & 0xF) | ((code[4 * i + 3] & 0xF) << 4);
+        d16[1 + i] = (uint16_t)(b0 | (b1 << 8));
+      }
     }
   }
 }
@@ -240,6 +250,7 @@ struct Group {
 template <int F> struct VBias;
 template <> struct VBias<MAB_KV_Q8> { static constexpr float kBias = 1152.f; };
 template <> struct VBias<MAB_KV_Q4> { static constexpr float kBias = 1032.f; };
+template <> struct VBias<MAB_KV_F16> { static constexpr float kBias = 0.f; };  // the values themselves
 
 template <int NB>
 __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
@@ -352,7 +363,11 @@ __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
 // VBias<F>::kBias (1152 + code, or 1032 + code for 4-bit codes).
 template <int F>
 __device__ inline half2_t lds_code_pair_biased(const uint8_t* base, int o0, int o1, int dv) {
-  if constexpr (F == MAB_KV_Q8) {
+  if constexpr (F == MAB_KV_F16) {  // fp16 values: value dv of each key
+    const uint32_t w = (uint32_t)*reinterpret_cast<const uint16_t*>(base + o0 + 2 * dv) |
+                       ((uint32_t)*reinterpret_cast<const uint16_t*>(base + o1 + 2 * dv) << 16);
+    return __builtin_bit_cast(half2_t, w);
+  } else if constexpr (F == MAB_KV_Q8) {
     const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
     return __builtin_bit_cast(half2_t, w ^ 0x64806480u);
   } else {
@@ -458,10 +473,15 @@ __device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
     const int b = m / kStepKeys, key = m % kStepKeys;
     const bool ok = key < nvalid;
     if (!isv) {
-      const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kKOff + key * L::kRecK + b * L::kBK);
-      reinterpret_cast<float*>(w + L::kSKOff)[m] = ok ? (float)__builtin_bit_cast(half_t, bits) * zc : 0.f;
+      float d = 1.f;  // the unquantized format has no scale
+      if constexpr (KF != MAB_KV_F16)
+        d = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(w + L::kKOff + key * L::kRecK +
+                                                                                  b * L::kBK));
+      reinterpret_cast<float*>(w + L::kSKOff)[m] = ok ? d * zc : 0.f;
     } else {
-      const uint16_t bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
+      uint16_t bits = 0x3C00u;  // fp16 1.0
+      if constexpr (VF != MAB_KV_F16)
+        bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
       reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = ok ? bits : (uint16_t)0;
     }
   }
@@ -486,7 +506,8 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       half8_t kc;
-      if constexpr (KF == MAB_KV_Q8) kc = lds_codes8_q8(w + L::kKOff, rec + b * L::kBK + 2 + 8 * j);
+      if constexpr (KF == MAB_KV_F16) kc = *reinterpret_cast<const half8_t*>(w + L::kKOff + rec + b * L::kBK + 16 * j);
+      else if constexpr (KF == MAB_KV_Q8) kc = lds_codes8_q8(w + L::kKOff, rec + b * L::kBK + 2 + 8 * j);
       else kc = lds_codes8_q4(w + L::kKOff, rec + b * L::kBK + 2 + 4 * j);
       const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, gr.q[b], float4_t{0.f, 0.f, 0.f, 0.f},
                                                                  0, 0, 0);
@@ -534,8 +555,10 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     const half4_t s0 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 4 * j);
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
     const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-    gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
+    if constexpr (VBias<VF>::kBias != 0.f) {
+      const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int dv = 16 * t2 + n;  // value index inside block b
@@ -543,8 +566,16 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
-        vp[e] = lds_code_pair_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + 2,
-                                         (ka + 1) * L::kRecV + b * L::kBV + 2, dv);
+        vp[e] = lds_code_pair_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
+                                         (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, dv);
+        if constexpr (VF == MAB_KV_F16) {
+          // f16 values of keys past the range are whatever the pool holds
+          // there (possibly NaN): zero them, as their weight is zero
+          if (tail) {
+            if (kbase + ka >= kend) vp[e][0] = (half_t)0.f;
+            if (kbase + ka + 1 >= kend) vp[e][1] = (half_t)0.f;
+          }
+        }
       }
       const half8_t vc = half8_t{vp[0][0], vp[0][1], vp[1][0], vp[1][1], vp[2][0], vp[2][1], vp[3][0], vp[3][1]};
       gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
@@ -577,7 +608,7 @@ struct ChunkTile {
 // values is stored in the order (0,2,4,6,1,3,5,7); Q and the output follow suit.
 template <int F>
 __device__ inline int value_of_slot(int p) {
-  if constexpr (F == MAB_KV_Q8) return p;
+  if constexpr (F != MAB_KV_Q4) return p;
   else return (p & ~7) | ((p & 3) << 1) | ((p & 4) >> 2);
 }
 
@@ -585,12 +616,18 @@ __device__ inline int value_of_slot(int p) {
 // one key of K or V), loaded as dwords from the 4-byte-aligned address at or
 // below the block (the block starts at byte 0 or 2 of w).
 struct ChunkRaw {
-  uint32_t w[9];
+  uint32_t w[16];  // 9 dwords of a quantized block, the 16 of an f16 block
 };
 
 template <int F>
 __device__ inline void chunk_raw_load_al(ChunkRaw& r, const uint32_t* base) {
-  if constexpr (F == MAB_KV_Q8) {
+  if constexpr (F == MAB_KV_F16) {  // 64-byte blocks: always 16-byte aligned
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(base + 4 * i);
+      r.w[4 * i] = x[0]; r.w[4 * i + 1] = x[1]; r.w[4 * i + 2] = x[2]; r.w[4 * i + 3] = x[3];
+    }
+  } else if constexpr (F == MAB_KV_Q8) {
     const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
     const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + 4);
     r.w[0] = x0[0]; r.w[1] = x0[1]; r.w[2] = x0[2]; r.w[3] = x0[3];
@@ -626,14 +663,26 @@ template <int NB, int KF, int VF, int SH>
 __device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid) {
   using T = ChunkTile<NB>;
   const int F = is_v ? VF : KF;
-  half_t d = __builtin_bit_cast(half_t, (uint16_t)raw_scale<SH>(r));
-  if (!valid) d = (half_t)0.f;
+  half_t d;
   half8_t out[4];
+  if (F == MAB_KV_F16) {  // the values themselves, scale 1
+    d = (half_t)1.f;
+    // a key past the range holds whatever the pool holds there (possibly
+    // NaN): zero its values, as a scale of 0 does for the quantized formats
 #pragma unroll
-  for (int g8 = 0; g8 < 4; ++g8) {
-    if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes<SH>(r, 2 * g8), raw_codes<SH>(r, 2 * g8 + 1));
-    else out[g8] = codes8_q4(raw_codes<SH>(r, g8));
+    for (int g8 = 0; g8 < 4; ++g8)
+      out[g8] = valid ? __builtin_bit_cast(half8_t, u32x4_t{r.w[4 * g8], r.w[4 * g8 + 1], r.w[4 * g8 + 2],
+                                                            r.w[4 * g8 + 3]})
+                      : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+    d = __builtin_bit_cast(half_t, (uint16_t)raw_scale<SH>(r));
+#pragma unroll
+    for (int g8 = 0; g8 < 4; ++g8) {
+      if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes<SH>(r, 2 * g8), raw_codes<SH>(r, 2 * g8 + 1));
+      else out[g8] = codes8_q4(raw_codes<SH>(r, g8));
+    }
   }
+  if (!valid) d = (half_t)0.f;
   half_t* row = (is_v ? t.v : t.k) + key * T::kStride + 32 * b;
   if (is_v) {
     const half8_t dv = half8_t{d, d, d, d, d, d, d, d};
@@ -973,10 +1022,12 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   lsum += __shfl_xor(lsum, 32);
   if (n >= G) return;
   // remove the code bias: o -= bias * (sum of the block's weights)
+  if constexpr (VBias<VF>::kBias != 0.f) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
+      for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
+  }
   // lane (n, j) holds dims 16t + 4j + [0,4) of query head g*G + n
   if (whole) {
     float* dst = a.out + ((int64_t)r0 * a.hq + g * G + n) * D + 4 * j;
@@ -1194,7 +1245,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
 #pragma unroll
     for (int dt = 0; dt < 2 * NB; ++dt) {
       const float4_t o = cw.o[rt][dt] * inv;
-      if constexpr (VF == MAB_KV_Q8) {
+      if constexpr (VF != MAB_KV_Q4) {  // natural value order
         *reinterpret_cast<float4_t*>(dst + 16 * dt + 4 * j) = o;
       } else {
 #pragma unroll
@@ -1251,7 +1302,9 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
   }
   constexpr int nw = HAS_CHUNK ? kMixedWaves : kDecodeWaves;
   const int wave = threadIdx.x >> 6;
-  decode_worker<NB, KF, VF, 2>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes, (b - a.n_chunk_items) * nw + wave);
+  // f16 stages are 16 KB (twice q8): one stage in flight instead of two
+  decode_worker<NB, KF, VF, KF == MAB_KV_F16 ? 1 : 2>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
+                                                      (b - a.n_chunk_items) * nw + wave);
 }
 
 template <int NB, int KF, int VF>
@@ -1470,7 +1523,7 @@ plan_kernel(AttnArgs a) {
 // Host side
 // ---------------------------------------------------------------------------
 
-bool fmt_ok(int32_t f) { return f == MAB_KV_Q8 || f == MAB_KV_Q4; }
+bool fmt_ok(int32_t f) { return f == MAB_KV_Q8 || f == MAB_KV_Q4 || f == MAB_KV_F16; }
 
 int check_layout(const mab_kv_layout* L) {
   if (!L) return MAB_ERR_NULL;
@@ -1479,6 +1532,7 @@ int check_layout(const mab_kv_layout* L) {
   if (L->num_pages < 1 || !fmt_ok(L->k_format) || !fmt_ok(L->v_format) || L->reserved) return MAB_ERR_SHAPE;
   if (L->head_dim != 64 && L->head_dim != 128) return MAB_ERR_UNSUPPORTED;
   if (L->num_q_heads / L->num_kv_heads > kMaxGroup) return MAB_ERR_UNSUPPORTED;
+  if ((L->k_format == MAB_KV_F16) != (L->v_format == MAB_KV_F16)) return MAB_ERR_UNSUPPORTED;
   return MAB_OK;
 }
 
@@ -1624,7 +1678,8 @@ void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
 
 template <int NB>
 void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st) {
-  if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st);
+  if (L->k_format == MAB_KV_F16) launch_attention<NB, MAB_KV_F16, MAB_KV_F16>(a, grid, st);
+  else if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st);
   else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st);
   else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st);
   else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st);
@@ -1635,7 +1690,7 @@ void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hi
 extern "C" {
 
 int32_t kv_block_bytes(int32_t format) {
-  return format == MAB_KV_Q8 ? 34 : format == MAB_KV_Q4 ? 18 : 0;
+  return format == MAB_KV_Q8 ? 34 : format == MAB_KV_Q4 ? 18 : format == MAB_KV_F16 ? 64 : 0;
 }
 
 int64_t kv_pool_bytes(const mab_kv_layout* layout, int32_t format) {
@@ -1666,7 +1721,8 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch, con
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)) return MAB_ERR_ALIGN;
   hipStream_t hs = (hipStream_t)stream;
   const int kf = layout->k_format, vf = layout->v_format;
-  if (kf == MAB_KV_Q8 && vf == MAB_KV_Q8) launch_append<MAB_KV_Q8, MAB_KV_Q8>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  if (kf == MAB_KV_F16) launch_append<MAB_KV_F16, MAB_KV_F16>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
+  else if (kf == MAB_KV_Q8 && vf == MAB_KV_Q8) launch_append<MAB_KV_Q8, MAB_KV_Q8>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
   else if (kf == MAB_KV_Q8) launch_append<MAB_KV_Q8, MAB_KV_Q4>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
   else if (vf == MAB_KV_Q8) launch_append<MAB_KV_Q4, MAB_KV_Q8>(layout, batch, k_new, v_new, k_pool, v_pool, hs);
   else launch_append<MAB_KV_Q4, MAB_KV_Q4>(layout, batch, k_new, v_new, k_pool, v_pool, hs);

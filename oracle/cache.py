@@ -4,7 +4,7 @@ A pool holds ``num_pages`` pages.  One page holds ``page_size`` consecutive
 token positions of one sequence for every KV head; within a page, the data of
 one KV head is contiguous.  Byte layout of a pool::
 
-    pool[num_pages][num_kv_heads][page_size][head_dim / 32][B]      B = 34 or 18
+    pool[num_pages][num_kv_heads][page_size][head_dim / 32][B]      B = 34, 18 or 64 (f16)
 
 The token at absolute position t of sequence s, KV head g, block b lives at
 ``pool[block_table[s][t // page_size], g, t % page_size, b]``.  Physical page

@@ -19,6 +19,11 @@ the 32 values as two's-complement bytes.  The payload of the 4-bit block is 16
 bytes; byte j holds value 2j in its low nibble and value 2j+1 in its high
 nibble, each as a two's-complement nibble.  Decoding is x_hat_i = q_i * d.
 
+The unquantized f16 mode of the same table (2 bytes per value; 2048 bytes per
+position in the occupancy table) is stored in the same block structure: a
+"block" is the 32 values themselves, 64 bytes of little-endian IEEE halves, with
+no scale; encoding and decoding are the identity on the fp16 values.
+
 Readings taken where the page is silent (each also listed in the design notes):
 the block runs along head_dim of one token and one KV head; the quantizing
 scale is the binary32 value s while the stored (and decoding) scale is its
@@ -35,16 +40,18 @@ import numpy as np
 
 VALUES_PER_BLOCK = 32
 
-#: format name -> (bytes per block, largest code magnitude)
+#: format name -> (bytes per block, largest code magnitude; None: unquantized)
 _FORMATS = {
     "q8": (2 + 32, 127),
     "q4": (2 + 16, 7),
+    "f16": (2 * 32, None),
 }
 
 
 def block_bytes(fmt):
     """Bytes of one 32-value block: 34 for q8, 18 for q4 (MBufo page, section 2,
-    KV modes table).  Pinned by the closed forms in the modes table."""
+    KV modes table), 64 for the unquantized f16 mode (2 bytes per value).
+    Pinned by the closed forms in the modes table and the occupancy table."""
     return _FORMATS[fmt][0]
 
 
@@ -94,6 +101,8 @@ def encode_blocks(x, fmt):
     x = np.asarray(x)
     assert x.dtype == np.float16 and x.shape[-1] == VALUES_PER_BLOCK
     nbytes, qm = _FORMATS[fmt]
+    if fmt == "f16":  # the values themselves, little-endian halves
+        return np.ascontiguousarray(x).astype("<f2").view(np.uint8).reshape(x.shape[:-1] + (nbytes,))
     qm32 = np.float32(qm)
 
     xf = x.astype(np.float32)                               # exact widening
@@ -126,7 +135,7 @@ def decode_codes(blocks, fmt):
     """Split blocks ``uint8[..., B]`` into (scale fp16[...], codes int8[..., 32])."""
     blocks = np.asarray(blocks, dtype=np.uint8)
     nbytes, _ = _FORMATS[fmt]
-    assert blocks.shape[-1] == nbytes
+    assert blocks.shape[-1] == nbytes and fmt != "f16"
     dbits = blocks[..., 0].astype(np.uint16) | (blocks[..., 1].astype(np.uint16) << 8)
     d = dbits.view(np.float16)
     payload = blocks[..., 2:]
@@ -150,5 +159,9 @@ def decode_blocks(blocks, fmt):
     significand is exact in binary64 (and in binary32).  Pinned by the worked
     examples and by the half-step bound against the encoder's input.
     """
+    if fmt == "f16":
+        blocks = np.ascontiguousarray(np.asarray(blocks, dtype=np.uint8))
+        assert blocks.shape[-1] == block_bytes("f16")
+        return blocks.view("<f2").astype(np.float64)
     d, q = decode_codes(blocks, fmt)
     return q.astype(np.float64) * d.astype(np.float64)[..., None]

@@ -24,6 +24,8 @@ Workloads (one attention layer each unless stated):
 * ``mixed16_chunk2k`` -- same heads and format: 16 decode rows with contexts in
                          [2048, 65536] plus a 2048-row chunk at position 131072
                          (of a 250000-token prompt); K outliers.
+* ``decode16_f16``    -- the decode16 batch (same seed, same contexts) over an
+                         unquantized f16 cache.
 * ``long_q8`` / ``long_k4v4`` -- one decode row at context 262144.
 * ``step_k4v4``       -- one layer of the full-step stress: K4V4, 16 decode rows
                          with contexts log-uniform in [512, 262144] and a
@@ -88,7 +90,7 @@ def _spec(name):
 
 def _draw_seqs(name, rng):
     """(prefix_len, q_len) per sequence for the named workload."""
-    if name == "decode16":
+    if name in ("decode16", "decode16_f16"):
         ctx = rng.integers(1024, 32768, size=16, endpoint=True)
         return [(int(c) - 1, 1) for c in ctx]
     if name == "mixed16_chunk2k":
@@ -107,6 +109,8 @@ def _heads_format(name):
         return dict(hq=24, hkv=4, d=128, kf="q8", vf="q8", ps=256)
     if name in ("long_k4v4", "step_k4v4"):
         return dict(hq=24, hkv=4, d=128, kf="q4", vf="q4", ps=256)
+    if name == "decode16_f16":
+        return dict(hq=24, hkv=4, d=128, kf="f16", vf="f16", ps=256)
     raise KeyError(name)
 
 
@@ -114,7 +118,7 @@ def _outlier_fraction(name):
     return 0.0 if name in ("long_q8", "long_k4v4") else OUTLIER_FRACTION
 
 
-WORKLOADS = ("tiny_mixed", "small_mixed", "decode16", "mixed16_chunk2k",
+WORKLOADS = ("tiny_mixed", "small_mixed", "decode16", "decode16_f16", "mixed16_chunk2k",
              "long_q8", "long_k4v4", "step_k4v4")
 
 

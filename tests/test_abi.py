@@ -34,8 +34,9 @@ def test_library_exports_every_declared_function():
 
 def test_block_and_pool_sizes():
     assert mab.kv_block_bytes("q8") == 34 and mab.kv_block_bytes("q4") == 18
+    assert mab.kv_block_bytes("f16") == 64
     assert mab.kv_block_bytes(99) == 0
-    for kf, vf in (("q8", "q8"), ("q4", "q4"), ("q8", "q4")):
+    for kf, vf in (("q8", "q8"), ("q4", "q4"), ("q8", "q4"), ("f16", "f16")):
         lay = mab.make_layout(24, 4, 128, 256, 77, kf, vf)
         d = dict(num_q_heads=24, num_kv_heads=4, head_dim=128, page_size=256, num_pages=77)
         assert mab.kv_pool_bytes(lay, kf) == oracle_cache.pool_bytes(d, kf)
@@ -127,7 +128,8 @@ def test_workspace_large_batch_holds_tables():
 
 @pytest.mark.parametrize("mutate,status", [
     (dict(num_q_heads=25), 2), (dict(head_dim=96), 3), (dict(head_dim=48), 2),
-    (dict(page_size=24), 2), (dict(page_size=0), 2), (dict(k_format=3), 2),
+    (dict(page_size=24), 2), (dict(page_size=0), 2), (dict(k_format=4), 2),
+    (dict(k_format=3), 3), (dict(v_format=3), 3),    # f16 on one side only
     (dict(num_q_heads=36, num_kv_heads=2), 3), (dict(num_pages=0), 2), (dict(reserved=1), 2),
 ])
 def test_layout_errors(mutate, status):

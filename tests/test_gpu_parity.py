@@ -35,6 +35,8 @@ CASES = {
     "g6_d128_p16": ("tiny_mixed", 6, dict(hq=12, hkv=2, d=128, ps=16)),
     "g8_d64": ("tiny_mixed", 7, dict(hq=8, hkv=1)),
     "g1_d64_p48": ("tiny_mixed", 8, dict(hq=2, hkv=2, ps=48)),
+    "small_f16": ("small_mixed", 9, dict(kf="f16", vf="f16")),
+    "tiny_f16_p48": ("tiny_mixed", 10, dict(kf="f16", vf="f16", ps=48)),
 }
 
 

@@ -38,6 +38,8 @@ def run_oracle(case, kp=None, vp=None, rows=None):
 # ---- pure-Python brute force (no numpy arithmetic, no vectorisation) --------------------
 
 def _py_decode_block(raw, fmt):
+    if fmt == "f16":  # 32 little-endian IEEE halves
+        return list(struct.unpack("<32e", bytes(int(b) for b in raw)))
     d = struct.unpack("<e", bytes([int(raw[0]), int(raw[1])]))[0]
     vals = []
     if fmt == "q8":
@@ -86,7 +88,7 @@ def brute_force(case, kp, vp):
     return np.array(out, dtype=np.float64)
 
 
-@pytest.mark.parametrize("kf,vf", [("q8", "q8"), ("q4", "q4"), ("q8", "q4"), ("q4", "q8")])
+@pytest.mark.parametrize("kf,vf", [("q8", "q8"), ("q4", "q4"), ("q8", "q4"), ("q4", "q8"), ("f16", "f16")])
 def test_brute_force_tiny(kf, vf):
     case = synth.make_case("tiny_mixed", seed=5, seqs=[(5, 3), (0, 2), (20, 1), (16, 1), (31, 1)],
                            hq=4, hkv=2, d=64, ps=16, kf=kf, vf=vf, outliers=0.05)
@@ -111,6 +113,30 @@ def test_codec_free_case_matches_torch_sdpa():
     mask = torch.from_numpy(np.arange(length)[None, :] <= pos[:, None])
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=sm)
     np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-10)
+
+
+def test_f16_cache_matches_torch_sdpa_on_the_raw_values():
+    # The unquantized f16 format through the whole paged, mixed-batch path
+    # (append, block table, causal chunk rows, decode rows) equals a library
+    # attention over the case's own fp16 K/V, with no codec in between.
+    case = synth.make_case("tiny_mixed", seed=9, seqs=[(40, 24), (0, 5), (77, 1), (15, 1)],
+                           hq=6, hkv=2, d=64, ps=16, kf="f16", vf="f16", outliers=0.05)
+    got = run_oracle(case)
+    lay = case.layout
+    hq, hkv = lay["num_q_heads"], lay["num_kv_heads"]
+    want = np.empty_like(got)
+    for s in range(case.num_seqs):
+        r0, r1 = int(case.q_start[s]), int(case.q_start[s + 1])
+        k = torch.cat([case.k_prefix[s].cpu(), case.k_new[r0:r1].cpu()]).double()   # [L, Hkv, D]
+        v = torch.cat([case.v_prefix[s].cpu(), case.v_new[r0:r1].cpu()]).double()
+        q = case.q[r0:r1].cpu().double()
+        pos = int(case.prefix_len[s]) + np.arange(r1 - r0)
+        mask = torch.from_numpy(np.arange(k.shape[0])[None, :] <= pos[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.permute(1, 0, 2)[None], k.permute(1, 0, 2).repeat_interleave(hq // hkv, 0)[None],
+            v.permute(1, 0, 2).repeat_interleave(hq // hkv, 0)[None], attn_mask=mask, scale=case.sm_scale)
+        want[r0:r1] = ref[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-10)
 
 
 def test_closed_forms():

@@ -1,5 +1,6 @@
 """Pins of the oracle's block codec against what the pages and IEEE arithmetic fix."""
 
+import struct
 from fractions import Fraction
 
 import numpy as np
@@ -129,6 +130,23 @@ def test_codec_invariants(fmt):
         for t, c, h in zip(xi, qi, xh):
             assert Fraction(float(h)) == c * dd                         # exact product
             assert abs(t - c * dd) <= s / 2 + abs(c) * abs(s - dd) + s / 2 ** 17
+
+
+def test_f16_block_is_the_little_endian_halves():
+    # The unquantized mode: a block is its 32 values as IEEE halves (struct's
+    # 'e' format is an independent encoder), 64 bytes, decoded exactly.
+    assert codec.block_bytes("f16") == 64 and codec.qmax("f16") is None
+    assert codec.bytes_per_position(4, 128, "f16", "f16") == 4 * 4 * codec.block_bytes("f16") * 2 == 2048
+    rng = np.random.default_rng(21)
+    x = _random_blocks(rng, 200)
+    x[0, :4] = np.array([0.0, -0.0, 6.0e-8, -65504.0], dtype=np.float16)   # zeros, a subnormal, the limit
+    b = codec.encode_blocks(x, "f16")
+    assert b.shape == (200, 64)
+    for i in range(len(x)):
+        assert bytes(b[i]) == struct.pack("<32e", *[float(t) for t in x[i]])
+    back = codec.decode_blocks(b, "f16")
+    assert np.array_equal(back, x.astype(np.float64))
+    assert np.array_equal(np.signbit(back[0, :2]), [False, True])
 
 
 def test_encode_shape_and_dtype_contract():
