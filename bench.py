@@ -40,13 +40,16 @@ WORKLOADS = {
                        "position 131072, 24/4 heads, head_dim 128, q8, page 256, K outliers, 1 layer",
     "decode16_f16": "the decode16 batch (16 decode rows, contexts uniform in [1024, 32768], 24/4 heads, "
                     "head_dim 128, page 256) over an unquantized f16 cache (64-byte blocks), 1 layer",
+    "verify16": "16 verify rows of 4 tokens each (contexts of the last token uniform in [1024, 32768]), "
+                "24/4 heads, head_dim 128, q8 34-byte blocks, page 256, 2% K outlier channels x20, 1 layer",
     "long_q8": "one decode row at context 262144, 24/4 heads, head_dim 128, q8, page 256, 1 layer",
     "long_k4v4": "one decode row at context 262144, 24/4 heads, head_dim 128, K4V4 18-byte blocks, "
                  "page 256, 1 layer",
     "step_k4v4": "12 attention layers, each: 16 decode rows (contexts log-uniform in [512, 262144]) + "
                  "a 2048-row chunk at 131072, 24/4 heads, head_dim 128, K4V4, page 256, K outliers",
 }
-SEEDS = {"decode16": 2, "decode16_f16": 2, "mixed16_chunk2k": 3, "long_q8": 4, "long_k4v4": 4, "step_k4v4": 5}
+SEEDS = {"decode16": 2, "decode16_f16": 2, "verify16": 6, "mixed16_chunk2k": 3, "long_q8": 4, "long_k4v4": 4,
+         "step_k4v4": 5}
 
 
 def kv_bytes_per_position(layout):
@@ -57,12 +60,14 @@ def kv_bytes_per_position(layout):
 
 
 def chunk_flops(case):
-    """QK^T and PV flops of the chunk rows over their visible keys (unmasked pairs)."""
+    """QK^T and PV flops of the prefill-chunk rows (sequences of more than 16
+    rows, the ones on the matrix-core tiles) over their visible keys (unmasked
+    pairs)."""
     lay = case.layout
     f = 0
     for s in range(case.num_seqs):
         n = case.q_len(s)
-        if n > 1:
+        if n > 16:
             p = int(case.prefix_len[s])
             f += 4 * lay["head_dim"] * lay["num_q_heads"] * (n * (p + 1) + n * (n - 1) // 2)
     return f

@@ -157,10 +157,12 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch,
  * operands on the matrix cores with fp32 accumulation, fp32 online softmax,
  * split-K over key ranges merged by log-sum-exp in fixed order.  The result
  * is deterministic (bit-identical run to run) and independent of the
- * physical page ids.  Rows of a chunk sequence (q_len > 1) are also
- * bit-identical whatever else shares the batch; a decode row's key range is
- * cut according to the whole batch, so it may differ in the last bits
- * (within 1e-3 at unit-scale values) between different batches.
+ * physical page ids.  Sequences of more than 16 rows (prefill chunks) get
+ * results that are also bit-identical whatever else shares the batch.  Shorter
+ * sequences (decode rows, and verify rows of 2-16 tokens, which run in groups
+ * of 16/(Hq/Hkv) rows on the decode path) have their key ranges cut according
+ * to the whole batch, so they may differ in the last bits (within 1e-3 at
+ * unit-scale values) between different batches.
  *
  * q          : device fp16 [num_rows][Hq][D], read only.
  * k_pool, v_pool : device pools, read only.

@@ -48,10 +48,12 @@ constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two 
 constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
 constexpr int kStepKeys = 32;       // keys per stage / tile
 constexpr int kMaxGroup = 8;        // query heads per KV head
+constexpr int kMaxVerify = 16;      // sequences with at most this many rows run on the decode path
 constexpr int kMaxSeqs = 4096;
 constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this many stages per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
+constexpr float kDecodeMaxFloor = -1e30f;  // initial running max of a decode slot (log2 units)
 
 template <int F> struct Fmt;
 template <> struct Fmt<MAB_KV_Q8> { static constexpr int kBytes = 34; static constexpr int kQmax = 127; };
@@ -68,6 +70,16 @@ __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a 
 // rows of one query head: H heads of the group (the largest of 4, 2, 1 that
 // divides G) times 256/H rows.  Its K/V steps are dequantized once for all.
 __host__ __device__ inline int chunk_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+// Rows of a sequence with q_len <= kMaxVerify (decode rows and short verify
+// rows) run on the decode path, in sub-rows of at most dec_tokens(G)
+// consecutive rows whose (row, head) pairs fill the 16 MFMA slots of a decode
+// wave; sub-row i holds rows [i*T, min(q_len, (i+1)*T)) and streams the keys
+// its last row sees.  Longer sequences are prefill chunks.
+__host__ __device__ inline bool is_chunk(int q_len) { return q_len > kMaxVerify; }
+__host__ __device__ inline int dec_tokens(int group) { return 16 / group; }
+__host__ __device__ inline int dec_subrows(int q_len, int group) {
+  return (q_len + dec_tokens(group) - 1) / dec_tokens(group);
+}
 __host__ __device__ inline int chunk_rows(int group) { return 32 * kMixedWaves / chunk_heads(group); }
 
 // A sequence with more than one row is a chunk: ceil(q_len/rows) row tiles x
@@ -109,7 +121,8 @@ struct DirEntry {
 };
 
 // Workspace: decode partials (slot = worker * pmax + piece; o fp32
-// [slot][G][D], (m, l) fp32 pairs [slot][G]), chunk partials of split tiles
+// [slot][P][D], (m, l) fp32 pairs [slot][P], P the (row, head) slots of a
+// decode sub-row), chunk partials of split tiles
 // (o fp32 [item][G][rows][D], (m, l) [item][G][rows]), one directory entry per
 // decode segment, and the launch-order tables for batches too large for the
 // kernel arguments.  Nothing needs initialising: every entry read is written
@@ -493,9 +506,11 @@ __device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
 // scale) with P rounded to fp16 once and multiplied by the fp16 V scale of
 // each block.  The V codes enter with the bias of their conversion; the sum
 // of each block's weights (an MFMA against ones) removes it at the end.
-// `tail`: the stage holds keys at or past kend (masked).
+// `tail`: the stage holds keys at or past kend, or past the limit of some
+// slot (masked per slot).
 template <int NB, int KF, int VF>
 __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, int lane) {
+  // keys visible to this lane's slot in the stage: below kend and at most gr.limit
   using L = DecLayout<NB, KF, VF>;
   const int j = lane >> 4, n = lane & 15;
   float4_t s[2];
@@ -520,7 +535,7 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (kbase + 16 * kt + 4 * j + i >= kend) s[kt][i] = -INFINITY;
+        if (kbase + 16 * kt + 4 * j + i >= min(kend, gr.limit + 1)) s[kt][i] = -INFINITY;
   }
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -856,14 +871,14 @@ constexpr int kArgDec = 96;
 constexpr int kArgChunk = 16;
 
 struct ArgTabs {
-  int dec_unit[kArgDec + 1], dec_seq[kArgDec], dec_r0[kArgDec], dec_ctx[kArgDec];
+  int dec_unit[kArgDec + 1], dec_seq[kArgDec], dec_r0[kArgDec], dec_ctx[kArgDec], dec_ntok[kArgDec];
   int ch_item[kArgChunk + 1], ch_seq[kArgChunk], ch_r0[kArgChunk], ch_qlen[kArgChunk], ch_prefix[kArgChunk];
   int ch_split[kArgChunk];
 };
 
 // Offsets (in ints) of the tables in the workspace.
 struct WsTabs {
-  int dec_unit, dec_seq, dec_r0, dec_ctx, ch_item, ch_seq, ch_r0, ch_qlen, ch_prefix, ch_split, total;
+  int dec_unit, dec_seq, dec_r0, dec_ctx, dec_ntok, ch_item, ch_seq, ch_r0, ch_qlen, ch_prefix, ch_split, total;
 };
 
 __host__ __device__ inline WsTabs ws_tabs(int n_dec, int n_chunk) {
@@ -873,6 +888,7 @@ __host__ __device__ inline WsTabs ws_tabs(int n_dec, int n_chunk) {
   t.dec_seq = o; o += n_dec;
   t.dec_r0 = o; o += n_dec;
   t.dec_ctx = o; o += n_dec;
+  t.dec_ntok = o; o += n_dec;
   t.ch_item = o; o += n_chunk + 1;
   t.ch_seq = o; o += n_chunk;
   t.ch_r0 = o; o += n_chunk;
@@ -905,13 +921,14 @@ struct AttnArgs {
   int dec_units;            // stages in the decode stream
   int dec_range;            // stages per decode worker (the last may have fewer)
   int dec_pmax;             // partial slots per decode worker
+  int dec_slots;            // (row, head) slots of a decode partial: G, or T*G with verify rows
   int tabs_in_ws;           // tables in the workspace (1) or in `tabs` (0)
   float c;                  // sm_scale * log2(e)
   ArgTabs tabs;
 };
 
 struct TabView {
-  const int *dec_unit, *dec_seq, *dec_r0, *dec_ctx;
+  const int *dec_unit, *dec_seq, *dec_r0, *dec_ctx, *dec_ntok;
   const int *ch_item, *ch_seq, *ch_r0, *ch_qlen, *ch_prefix, *ch_split;
 };
 
@@ -921,11 +938,13 @@ __device__ inline TabView tab_view(const AttnArgs& a) {
     const WsTabs t = ws_tabs(a.n_dec, a.n_chunk);
     const int* b = a.ws_tab;
     v.dec_unit = b + t.dec_unit; v.dec_seq = b + t.dec_seq; v.dec_r0 = b + t.dec_r0; v.dec_ctx = b + t.dec_ctx;
+    v.dec_ntok = b + t.dec_ntok;
     v.ch_item = b + t.ch_item; v.ch_seq = b + t.ch_seq; v.ch_r0 = b + t.ch_r0; v.ch_qlen = b + t.ch_qlen;
     v.ch_prefix = b + t.ch_prefix;
     v.ch_split = b + t.ch_split;
   } else {
     v.dec_unit = a.tabs.dec_unit; v.dec_seq = a.tabs.dec_seq; v.dec_r0 = a.tabs.dec_r0; v.dec_ctx = a.tabs.dec_ctx;
+    v.dec_ntok = a.tabs.dec_ntok;
     v.ch_item = a.tabs.ch_item; v.ch_seq = a.tabs.ch_seq; v.ch_r0 = a.tabs.ch_r0; v.ch_qlen = a.tabs.ch_qlen;
     v.ch_prefix = a.tabs.ch_prefix;
     v.ch_split = a.tabs.ch_split;
@@ -956,14 +975,15 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
   }
 }
 
-// One piece of a decode segment (row r0 of sequence s, KV head g, keys
-// [kb, ke), kb a multiple of 32), streamed by one wave: 32-key stages, DEPTH
+// One piece of a decode segment (ntok rows from row r0 of sequence s, the
+// last of which sees ctx keys, KV head g, keys [kb, ke), kb a multiple of 32),
+// streamed by one wave; slot n of the wave is row r0 + n/G, head g*G + n%G: 32-key stages, DEPTH
 // stages ahead, with loads that bypass the caches' retention (every byte is
 // read once), through the wave's own LDS stage buffer wbuf.  A whole segment
 // writes the output, a piece its partial at `slot`.
 template <int NB, int KF, int VF, int DEPTH>
-__device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int r0, int ctx, int g, int kb,
-                                    int ke, bool whole, int64_t slot) {
+__device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int r0, int ntok, int ctx, int g,
+                                    int kb, int ke, bool whole, int64_t slot) {
   constexpr int D = 32 * NB;
   const int lane = threadIdx.x & 63;
   const int G = a.hq / a.hkv;
@@ -982,8 +1002,15 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
     return key < ke ? gload_i32(ic.bt_row + key / a.page_size) : 0;
   };
   int my_page = page_window(0);
+  const int tn = n / G, hn = n % G;  // this lane's slot: row r0 + tn, head g*G + hn
+  const bool live = tn < ntok;
+  const int64_t orow = (int64_t)(r0 + tn) * a.hq + g * G + hn;
   Group<NB> gr;
-  dec_init<NB, KF>(gr, n < G ? a.q + ((int64_t)r0 * a.hq + g * G + n) * D : nullptr, ctx - 1, lane);
+  dec_init<NB, KF>(gr, live ? a.q + orow * D : nullptr, ctx - ntok + tn, lane);
+  // a finite floor for the running max: a verify row's slot may see no key of
+  // a piece that starts past its limit, and exp2(-inf - floor) is 0, not NaN
+  gr.m = kDecodeMaxFloor;
+  const int kvis = min(ke, ctx - ntok + 1);  // keys below this are visible to every live slot
   // DEPTH register sets: stage st is consumed from set st % DEPTH while the
   // next DEPTH-1 stages load into the others; its set is refilled with stage
   // st + DEPTH as soon as it is in LDS
@@ -1006,7 +1033,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
     dec_scales<NB, KF, VF>(wbuf, lane, a.c, ke - kbase);
     if (st + DEPTH < nst) issue(dw, st + DEPTH);
     asm volatile("" ::: "memory");
-    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > ke, lane);
+    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > kvis, lane);
     asm volatile("" ::: "memory");
   };
 #pragma unroll
@@ -1020,7 +1047,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  if (n >= G) return;
+  if (!live) return;
   // remove the code bias: o -= bias * (sum of the block's weights)
   if constexpr (VBias<VF>::kBias != 0.f) {
 #pragma unroll
@@ -1028,14 +1055,14 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
   }
-  // lane (n, j) holds dims 16t + 4j + [0,4) of query head g*G + n
+  // lane (n, j) holds dims 16t + 4j + [0,4) of slot n
   if (whole) {
-    float* dst = a.out + ((int64_t)r0 * a.hq + g * G + n) * D + 4 * j;
+    float* dst = a.out + orow * D + 4 * j;
     const float inv = 1.f / lsum;
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t] * inv;
   } else {
-    const int64_t pi = slot * G + n;
+    const int64_t pi = slot * a.dec_slots + n;
     float* dst = a.o_part + pi * D + 4 * j;
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t];
@@ -1055,7 +1082,7 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
   int e = wave_find(tv.dec_unit, a.n_dec, x0);
   int x = x0, k = 0;
   while (x < x1) {
-    const int ctx = tv.dec_ctx[e], ub = tv.dec_unit[e];
+    const int ctx = tv.dec_ctx[e], ub = tv.dec_unit[e], ntok = tv.dec_ntok[e];
     const int nst = dec_stages(ctx);
     const int g = (x - ub) / nst;
     const int seg_lo = ub + g * nst, seg_hi = seg_lo + nst;
@@ -1063,7 +1090,7 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
     const int r0 = tv.dec_r0[e];
     const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
     const int64_t slot = (int64_t)w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF, DEPTH>(a, wbuf, tv.dec_seq[e], r0, ctx, g, (x - seg_lo) * kStepKeys,
+    decode_piece<NB, KF, VF, DEPTH>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
                                     min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
     if (first && (threadIdx.x & 63) == 0) {
       DirEntry d;
@@ -1339,7 +1366,8 @@ decode_attention_kernel(AttnArgs a) {
 }
 
 // Merges the pieces of decode segments that span several decode workers.
-// One work-group per (segment, query head of the group, 32 dims): thread
+// One work-group per (segment, slot, 32 dims), slot n being row n/G of the
+// segment's sub-row and query head n%G of the group: thread
 // (phase ph, dim) folds pieces ph, ph+P, ph+2P, ... into a running (m, l, o)
 // with up to sixteen loads in flight, then the P phases are folded pairwise in
 // a fixed tree.  P = 8, or 32 when some segment has more than
@@ -1362,12 +1390,13 @@ __global__ void __launch_bounds__(32 * P)
 combine_kernel(AttnArgs a, int head_dim) {
   constexpr int kCombinePhases = P;
   __shared__ float red[3][32 * P];
-  const int G = a.hq / a.hkv, ndg = head_dim / 32;
-  const int seg = blockIdx.x / (G * ndg), rem = blockIdx.x % (G * ndg);
+  const int G = a.hq / a.hkv, S = a.dec_slots, ndg = head_dim / 32;
+  const int seg = blockIdx.x / (S * ndg), rem = blockIdx.x % (S * ndg);
   const int hl = rem / ndg, dd = (rem % ndg) * 32 + (threadIdx.x & 31);
   const int ph = threadIdx.x >> 5;
   const DirEntry d = a.dir[seg];
-  if (d.n <= 1) return;
+  const int ntok = tab_view(a).dec_ntok[seg / a.hkv];
+  if (d.n <= 1 || hl >= ntok * G) return;  // one piece, or a slot past the sub-row's rows
   auto slot = [&](int p) -> int64_t { return p == 0 ? d.slot : (int64_t)(d.wg + p) * a.dec_pmax; };
   float m = -INFINITY, l = 0.f, o = 0.f;
   for (int p0 = ph; p0 < d.n; p0 += kCombinePhases * kCombineUnroll) {
@@ -1379,7 +1408,7 @@ combine_kernel(AttnArgs a, int head_dim) {
       ml[u] = make_float2(-INFINITY, 0.f);
       ov[u] = 0.f;
       if (p < d.n) {
-        const int64_t pi = slot(p) * G + hl;
+        const int64_t pi = slot(p) * S + hl;
         ml[u] = a.ml_part[pi];
         ov[u] = a.o_part[pi * head_dim + dd];
       }
@@ -1399,7 +1428,7 @@ combine_kernel(AttnArgs a, int head_dim) {
     }
     __syncthreads();
   }
-  if (ph == 0) a.out[((int64_t)d.rh0 + hl) * head_dim + dd] = o / l;
+  if (ph == 0) a.out[((int64_t)d.rh0 + (int64_t)(hl / G) * a.hq + hl % G) * head_dim + dd] = o / l;
 }
 
 // Merges the key splits of chunk tiles cut into more than one split.  A tile
@@ -1468,12 +1497,16 @@ plan_kernel(AttnArgs a) {
   int v[4] = {0, 0, 0, 0};  // decode entries, decode units, chunk entries, chunk items
   for (int s = s0; s < s1; ++s) {
     const int q_len = a.q_start[s + 1] - a.q_start[s], ctx = a.prefix_len[s] + q_len;
-    if (q_len > 1) {
+    if (is_chunk(q_len)) {
       const int tiles = chunk_tiles(q_len, a.hkv, G);
       v[2] += 1;
       v[3] += tiles * chunk_split(tiles, a.ch_target);
+    } else {
+      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+        v[0] += 1;
+        v[1] += a.hkv * dec_stages(ctx - q_len + min(q_len, (i + 1) * T));
+      }
     }
-    else { v[0] += 1; v[1] += a.hkv * dec_stages(ctx); }
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) scan[k][tid] = v[k];
@@ -1494,7 +1527,7 @@ plan_kernel(AttnArgs a) {
   int* w = a.ws_tab;
   for (int s = s0; s < s1; ++s) {
     const int r0 = a.q_start[s], q_len = a.q_start[s + 1] - r0, prefix = a.prefix_len[s];
-    if (q_len > 1) {
+    if (is_chunk(q_len)) {
       const int c = base[2]++;
       w[t.ch_item + c] = base[3];
       w[t.ch_seq + c] = s;
@@ -1505,12 +1538,15 @@ plan_kernel(AttnArgs a) {
       w[t.ch_split + c] = f;
       base[3] += tiles * f;
     } else {
-      const int e = base[0]++;
-      w[t.dec_unit + e] = base[1];
-      w[t.dec_seq + e] = s;
-      w[t.dec_r0 + e] = r0;
-      w[t.dec_ctx + e] = prefix + 1;
-      base[1] += a.hkv * dec_stages(prefix + 1);
+      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+        const int e = base[0]++, t1 = min(q_len, (i + 1) * T);
+        w[t.dec_unit + e] = base[1];
+        w[t.dec_seq + e] = s;
+        w[t.dec_r0 + e] = r0 + i * T;
+        w[t.dec_ctx + e] = prefix + t1;
+        w[t.dec_ntok + e] = t1 - i * T;
+        base[1] += a.hkv * dec_stages(prefix + t1);
+      }
     }
   }
   if (tid == kPlanThreads - 1) {
@@ -1541,6 +1577,7 @@ struct HostPlan {
   bool ch_splits = false;  // some chunk tile is cut into several splits
   int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
   int dec_seg_pieces = 1;  // pieces of the most cut decode segment
+  int dec_slots = 1;       // (row, head) slots per decode partial
   int64_t n_slots = 0;
 };
 
@@ -1564,7 +1601,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   const int cus = device_cus();
   const int ch_target = cus;  // resident chunk work-groups: one per compute unit
   int64_t items = 0, units = 0;
-  int n_dec = 0, n_chunk = 0;
+  int n_dec = 0, n_chunk = 0, max_ntok = 1;
   bool ch_splits = false;
   for (int s = 0; s < B->num_seqs; ++s) {
     const int64_t q_len = (int64_t)B->q_start_host[s + 1] - B->q_start_host[s];
@@ -1572,13 +1609,18 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     if (q_len < 1 || prefix < 0) return MAB_ERR_SHAPE;
     const int64_t ctx = prefix + q_len;
     if (ctx > (int64_t)B->max_pages_per_seq * L->page_size || ctx > (int64_t)1 << 30) return MAB_ERR_SHAPE;
-    if (q_len > 1) {
+    if (is_chunk((int)q_len)) {
       const int tiles = chunk_tiles((int)q_len, hkv, G), f = chunk_split(tiles, ch_target);
       ++n_chunk;
       items += (int64_t)tiles * f;
       ch_splits |= f > 1;
+    } else {
+      const int T = dec_tokens(G), nsub = dec_subrows((int)q_len, G);
+      for (int i = 0; i < nsub; ++i)
+        units += (int64_t)hkv * dec_stages((int)(prefix + std::min<int64_t>(q_len, (int64_t)(i + 1) * T)));
+      n_dec += nsub;
+      max_ntok = std::max<int>(max_ntok, (int)std::min<int64_t>(q_len, T));
     }
-    else { ++n_dec; units += (int64_t)hkv * dec_stages((int)ctx); }
   }
   if (items > (int64_t)1 << 30 || units > (int64_t)1 << 30) return MAB_ERR_UNSUPPORTED;
   if (!hp) return MAB_OK;
@@ -1588,6 +1630,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->ch_target = ch_target;
   hp->ch_splits = ch_splits;
   hp->dec_units = (int)units;
+  hp->dec_slots = max_ntok * G;
   if (units > 0) {
     // equal ranges, one per decode worker (a wave), as many as the device
     // holds at once (eight waves per compute unit: two 4-wave work-groups of
@@ -1605,11 +1648,13 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     int64_t x = 0;
     for (int s = 0; s < B->num_seqs; ++s) {
       const int q_len = B->q_start_host[s + 1] - B->q_start_host[s];
-      if (q_len > 1) continue;
-      const int nst = dec_stages(B->prefix_len_host[s] + 1);
+      if (is_chunk(q_len)) continue;
+      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+      const int nst = dec_stages(B->prefix_len_host[s] + std::min(q_len, (i + 1) * T));
       for (int g = 0; g < hkv; ++g, x += nst) {
         if (x % range != 0) ++pieces[(size_t)(x / range)];
         hp->dec_seg_pieces = std::max<int>(hp->dec_seg_pieces, (int)((x + nst - 1) / range - x / range + 1));
+      }
       }
     }
     hp->dec_pmax = *std::max_element(pieces.begin(), pieces.end());
@@ -1622,7 +1667,7 @@ WsLayout plan_ws(const mab_kv_layout* L, const HostPlan& hp) {
   const int G = L->num_q_heads / L->num_kv_heads;
   const bool big = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
   const int64_t chunk_rows_total = hp.ch_splits ? (int64_t)hp.n_chunk_items * chunk_heads(G) * chunk_rows(G) : 0;
-  return ws_layout(hp.n_slots, G, L->head_dim, chunk_rows_total, (int64_t)hp.n_dec * L->num_kv_heads,
+  return ws_layout(hp.n_slots, hp.dec_slots, L->head_dim, chunk_rows_total, (int64_t)hp.n_dec * L->num_kv_heads,
                    big ? ws_tabs(hp.n_dec, hp.n_chunk).total : 0);
 }
 
@@ -1634,7 +1679,7 @@ void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
   int e = 0, c = 0, unit = 0, item = 0;
   for (int s = 0; s < B->num_seqs; ++s) {
     const int r0 = B->q_start_host[s], q_len = B->q_start_host[s + 1] - r0, prefix = B->prefix_len_host[s];
-    if (q_len > 1) {
+    if (is_chunk(q_len)) {
       a->tabs.ch_item[c] = item;
       a->tabs.ch_seq[c] = s;
       a->tabs.ch_r0[c] = r0;
@@ -1645,12 +1690,15 @@ void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
       item += tiles * f;
       ++c;
     } else {
-      a->tabs.dec_unit[e] = unit;
-      a->tabs.dec_seq[e] = s;
-      a->tabs.dec_r0[e] = r0;
-      a->tabs.dec_ctx[e] = prefix + 1;
-      unit += hkv * dec_stages(prefix + 1);
-      ++e;
+      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i, ++e) {
+        const int t1 = std::min(q_len, (i + 1) * T);
+        a->tabs.dec_unit[e] = unit;
+        a->tabs.dec_seq[e] = s;
+        a->tabs.dec_r0[e] = r0 + i * T;
+        a->tabs.dec_ctx[e] = prefix + t1;
+        a->tabs.dec_ntok[e] = t1 - i * T;
+        unit += hkv * dec_stages(prefix + t1);
+      }
     }
   }
   a->tabs.dec_unit[e] = unit;
@@ -1772,6 +1820,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   a.dec_units = hp.dec_units;
   a.dec_range = hp.dec_range;
   a.dec_pmax = hp.dec_pmax;
+  a.dec_slots = hp.dec_slots;
   a.c = sm_scale * kLog2e;
   a.tabs_in_ws = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
   hipStream_t hs = (hipStream_t)stream;
@@ -1791,8 +1840,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
     if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   }
   if (hp.n_dec > 0) {
-    const int G = layout->num_q_heads / layout->num_kv_heads;
-    const dim3 cgrid(hp.n_dec * layout->num_kv_heads * G * (layout->head_dim / 32));
+    const dim3 cgrid(hp.n_dec * layout->num_kv_heads * hp.dec_slots * (layout->head_dim / 32));
     if (hp.dec_seg_pieces > kCombineWidePieces)
       hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(32 * 32), 0, hs, a, layout->head_dim);
     else

@@ -26,6 +26,9 @@ Workloads (one attention layer each unless stated):
                          (of a 250000-token prompt); K outliers.
 * ``decode16_f16``    -- the decode16 batch (same seed, same contexts) over an
                          unquantized f16 cache.
+* ``verify16``        -- 16 verify rows of 4 tokens (speculative verify), the
+                         last token's context uniform in [1024, 32768]; decode16's
+                         heads and format, K outliers.
 * ``long_q8`` / ``long_k4v4`` -- one decode row at context 262144.
 * ``step_k4v4``       -- one layer of the full-step stress: K4V4, 16 decode rows
                          with contexts log-uniform in [512, 262144] and a
@@ -93,6 +96,9 @@ def _draw_seqs(name, rng):
     if name in ("decode16", "decode16_f16"):
         ctx = rng.integers(1024, 32768, size=16, endpoint=True)
         return [(int(c) - 1, 1) for c in ctx]
+    if name == "verify16":
+        ctx = rng.integers(1024, 32768, size=16, endpoint=True)
+        return [(int(c) - 4, 4) for c in ctx]
     if name == "mixed16_chunk2k":
         ctx = rng.integers(2048, 65536, size=16, endpoint=True)
         return [(131072, 2048)] + [(int(c) - 1, 1) for c in ctx]
@@ -105,7 +111,7 @@ def _draw_seqs(name, rng):
 
 
 def _heads_format(name):
-    if name in ("decode16", "mixed16_chunk2k", "long_q8"):
+    if name in ("decode16", "verify16", "mixed16_chunk2k", "long_q8"):
         return dict(hq=24, hkv=4, d=128, kf="q8", vf="q8", ps=256)
     if name in ("long_k4v4", "step_k4v4"):
         return dict(hq=24, hkv=4, d=128, kf="q4", vf="q4", ps=256)
@@ -118,7 +124,7 @@ def _outlier_fraction(name):
     return 0.0 if name in ("long_q8", "long_k4v4") else OUTLIER_FRACTION
 
 
-WORKLOADS = ("tiny_mixed", "small_mixed", "decode16", "decode16_f16", "mixed16_chunk2k",
+WORKLOADS = ("tiny_mixed", "small_mixed", "decode16", "decode16_f16", "verify16", "mixed16_chunk2k",
              "long_q8", "long_k4v4", "step_k4v4")
 
 

@@ -14,7 +14,7 @@ from gpu_harness import GpuState, assert_close, oracle_out, oracle_pools
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = [("decode16", 2), ("decode16_f16", 2), ("mixed16_chunk2k", 3), ("long_q8", 4),
+WORKLOADS = [("decode16", 2), ("decode16_f16", 2), ("verify16", 6), ("mixed16_chunk2k", 3), ("long_q8", 4),
              ("long_k4v4", 4), ("step_k4v4", 5)]
 
 

@@ -37,6 +37,15 @@ CASES = {
     "g1_d64_p48": ("tiny_mixed", 8, dict(hq=2, hkv=2, ps=48)),
     "small_f16": ("small_mixed", 9, dict(kf="f16", vf="f16")),
     "tiny_f16_p48": ("tiny_mixed", 10, dict(kf="f16", vf="f16", ps=48)),
+    # verify rows (2-16 tokens) run on the decode path in groups of 16/G rows;
+    # 17 rows is the shortest prefill chunk
+    "verify_g6": ("small_mixed", 11, dict(seqs=[(300, 2), (1000, 4), (5, 16), (0, 3), (77, 1), (2000, 7),
+                                                 (64, 17)])),
+    "verify_g1_p48": ("tiny_mixed", 12, dict(hq=2, hkv=2, ps=48, seqs=[(100, 16), (31, 5), (0, 2), (500, 1),
+                                                                          (47, 9)])),
+    "verify_g8_k4v4": ("tiny_mixed", 13, dict(hq=8, hkv=1, kf="q4", vf="q4", seqs=[(200, 9), (40, 2), (1, 1),
+                                                                                      (0, 16)])),
+    "verify_f16": ("small_mixed", 14, dict(kf="f16", vf="f16", seqs=[(129, 5), (0, 2), (640, 16), (33, 1)])),
 }
 
 
@@ -91,7 +100,7 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("key", ["tiny_mixed", "small_q8"])
+@pytest.mark.parametrize("key", ["tiny_mixed", "small_q8", "verify_g6"])
 def test_mixed_equals_separate(key):
     """One mixed launch versus launches of its parts.  Chunk rows are computed
     by work items that depend only on their own sequence: bitwise equal.  Decode
@@ -105,8 +114,8 @@ def test_mixed_equals_separate(key):
     st = GpuState(case)
     st.append_step()
     full = st.attention().cpu().numpy()
-    chunks = [s for s in range(case.num_seqs) if case.q_len(s) > 1]
-    decodes = [s for s in range(case.num_seqs) if case.q_len(s) == 1]
+    chunks = [s for s in range(case.num_seqs) if case.q_len(s) > 16]
+    decodes = [s for s in range(case.num_seqs) if case.q_len(s) <= 16]
     for seqs in (chunks, decodes, [decodes[-1], chunks[0]]):
         sub, rows = synth.subset(case, seqs)
         b = batch_of(sub.q_start, sub.prefix_len, sub.block_table)
@@ -114,7 +123,7 @@ def test_mixed_equals_separate(key):
         for k, s in enumerate(seqs):
             r_full = np.arange(case.q_start[s], case.q_start[s + 1])
             r_part = np.arange(sub.q_start[k], sub.q_start[k + 1])
-            if case.q_len(s) > 1:
+            if case.q_len(s) > 16:
                 assert np.array_equal(part[r_part], full[r_full]), f"chunk seq {s} of {seqs}"
             else:
                 d = float(np.abs(part[r_part] - full[r_full]).max())
@@ -136,6 +145,25 @@ def test_split_and_tile_boundaries(kf, vf):
     kp, vp = oracle_pools(case)
     want = oracle_out(case, kp, vp)
     assert_close(out, want, f"boundaries {kf}{vf}")
+
+
+def test_verify_rows_with_stage_aligned_limits():
+    """Verify rows whose first row sees exactly m whole stages: the stage after
+    them is visible only to the later rows, so a decode worker whose range
+    starts there has slots with no visible key in its piece.  Many such
+    segments of different lengths make the cut land there; the outputs must
+    match the oracle (no NaN from an empty piece)."""
+    rng = np.random.default_rng(51)
+    seqs = [(32 * int(rng.integers(1, 40)) - 1, int(rng.integers(2, 6))) for _ in range(40)]
+    seqs += [(int(rng.integers(0, 300)), 1) for _ in range(8)]
+    case = synth.make_case("small_mixed", 52, device="cuda", seqs=seqs, ps=32, spare_pages=4)
+    _say(f"stage-aligned verify rows: {len(seqs)} sequences, {case.num_rows} rows")
+    st = GpuState(case)
+    st.append_step()
+    out = st.attention().cpu().numpy()
+    assert np.isfinite(out).all()
+    kp, vp = oracle_pools(case)
+    assert_close(out, oracle_out(case, kp, vp), "stage-aligned verify rows")
 
 
 def test_large_batch_tables_in_workspace():
