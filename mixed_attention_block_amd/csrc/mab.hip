@@ -1366,17 +1366,18 @@ decode_attention_kernel(AttnArgs a) {
 }
 
 // Merges the pieces of decode segments that span several decode workers.
-// One work-group per (segment, slot, 32 dims), slot n being row n/G of the
-// segment's sub-row and query head n%G of the group: thread
-// (phase ph, dim) folds pieces ph, ph+P, ph+2P, ... into a running (m, l, o)
-// with up to sixteen loads in flight, then the P phases are folded pairwise in
-// a fixed tree.  P = 8, or 32 when some segment has more than
-// kCombineWidePieces pieces.  The order depends only on the piece count and
-// P: deterministic.
+// One work-group per (segment, slot, 1/SPLIT of the dims), slot n being row
+// n/G of the segment's sub-row and query head n%G of the group: thread (phase
+// ph, dims 4q..4q+3) folds pieces ph, ph+P, ph+2P, ... into a running
+// (m, l, o) with up to sixteen 16-byte loads in flight, then the P phases are
+// folded pairwise in a fixed tree.  P = 8 over all dims, or, when some
+// segment has more than kCombineWidePieces pieces (few long rows), P = 32
+// over 32 dims per work-group.  The order depends only on the piece count
+// and P: deterministic.
 constexpr int kCombineUnroll = 16;
 constexpr int kCombineWidePieces = 128;
 
-__device__ inline void lse_fold(float& m, float& l, float& o, float m2, float l2, float o2) {
+__device__ inline void lse_fold(float& m, float& l, float4_t& o, float m2, float l2, float4_t o2) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;  // both empty
   const float a1 = __builtin_amdgcn_exp2f(m - mn), a2 = __builtin_amdgcn_exp2f(m2 - mn);
@@ -1385,50 +1386,54 @@ __device__ inline void lse_fold(float& m, float& l, float& o, float m2, float l2
   m = mn;
 }
 
-template <int P>
-__global__ void __launch_bounds__(32 * P)
-combine_kernel(AttnArgs a, int head_dim) {
-  constexpr int kCombinePhases = P;
-  __shared__ float red[3][32 * P];
-  const int G = a.hq / a.hkv, S = a.dec_slots, ndg = head_dim / 32;
-  const int seg = blockIdx.x / (S * ndg), rem = blockIdx.x % (S * ndg);
-  const int hl = rem / ndg, dd = (rem % ndg) * 32 + (threadIdx.x & 31);
-  const int ph = threadIdx.x >> 5;
+template <int P, int NB, int SPLIT>
+__global__ void __launch_bounds__(8 * NB / SPLIT * P)
+combine_kernel(AttnArgs a) {
+  constexpr int DQ = 8 * NB / SPLIT, D = 32 * NB;  // threads per phase (four dims each), head_dim
+  __shared__ float4_t red_o[DQ * P];
+  __shared__ float2 red_ml[DQ * P];
+  const int G = a.hq / a.hkv, S = a.dec_slots;
+  const int wg = blockIdx.x / SPLIT, part = blockIdx.x % SPLIT;
+  const int seg = wg / S, hl = wg % S;
+  const int q4 = part * DQ + threadIdx.x % DQ, ph = threadIdx.x / DQ;
   const DirEntry d = a.dir[seg];
   const int ntok = tab_view(a).dec_ntok[seg / a.hkv];
   if (d.n <= 1 || hl >= ntok * G) return;  // one piece, or a slot past the sub-row's rows
   auto slot = [&](int p) -> int64_t { return p == 0 ? d.slot : (int64_t)(d.wg + p) * a.dec_pmax; };
-  float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int p0 = ph; p0 < d.n; p0 += kCombinePhases * kCombineUnroll) {
+  float m = -INFINITY, l = 0.f;
+  float4_t o = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = ph; p0 < d.n; p0 += P * kCombineUnroll) {
     float2 ml[kCombineUnroll];
-    float ov[kCombineUnroll];
+    float4_t ov[kCombineUnroll];
 #pragma unroll
     for (int u = 0; u < kCombineUnroll; ++u) {
-      const int p = p0 + kCombinePhases * u;
+      const int p = p0 + P * u;
       ml[u] = make_float2(-INFINITY, 0.f);
-      ov[u] = 0.f;
+      ov[u] = float4_t{0.f, 0.f, 0.f, 0.f};
       if (p < d.n) {
         const int64_t pi = slot(p) * S + hl;
         ml[u] = a.ml_part[pi];
-        ov[u] = a.o_part[pi * head_dim + dd];
+        ov[u] = *reinterpret_cast<const float4_t*>(a.o_part + pi * D + 4 * q4);
       }
     }
 #pragma unroll
     for (int u = 0; u < kCombineUnroll; ++u) lse_fold(m, l, o, ml[u].x, ml[u].y, ov[u]);
   }
   // fixed pairwise tree over the phases: phase ph takes phase ph + half
-  for (int half = kCombinePhases / 2; half >= 1; half >>= 1) {
-    red[0][threadIdx.x] = m;
-    red[1][threadIdx.x] = l;
-    red[2][threadIdx.x] = o;
+  for (int half = P / 2; half >= 1; half >>= 1) {
+    red_o[threadIdx.x] = o;
+    red_ml[threadIdx.x] = make_float2(m, l);
     __syncthreads();
     if (ph < half) {
-      const int t = threadIdx.x + 32 * half;
-      lse_fold(m, l, o, red[0][t], red[1][t], red[2][t]);
+      const int t = threadIdx.x + DQ * half;
+      const float2 ml2 = red_ml[t];
+      lse_fold(m, l, o, ml2.x, ml2.y, red_o[t]);
     }
     __syncthreads();
   }
-  if (ph == 0) a.out[((int64_t)d.rh0 + (int64_t)(hl / G) * a.hq + hl % G) * head_dim + dd] = o / l;
+  if (ph == 0)
+    *reinterpret_cast<float4_t*>(a.out + ((int64_t)d.rh0 + (int64_t)(hl / G) * a.hq + hl % G) * D + 4 * q4) =
+        o / l;
 }
 
 // Merges the key splits of chunk tiles cut into more than one split.  A tile
@@ -1840,11 +1845,15 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
     if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   }
   if (hp.n_dec > 0) {
-    const dim3 cgrid(hp.n_dec * layout->num_kv_heads * hp.dec_slots * (layout->head_dim / 32));
-    if (hp.dec_seg_pieces > kCombineWidePieces)
-      hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(32 * 32), 0, hs, a, layout->head_dim);
-    else
-      hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(32 * 8), 0, hs, a, layout->head_dim);
+    const int nwg = hp.n_dec * layout->num_kv_heads * hp.dec_slots;
+    const bool wide = hp.dec_seg_pieces > kCombineWidePieces;
+    if (layout->head_dim == 64) {
+      if (wide) hipLaunchKernelGGL((combine_kernel<32, 2, 2>), dim3(nwg * 2), dim3(32 * 8), 0, hs, a);
+      else hipLaunchKernelGGL((combine_kernel<8, 2, 1>), dim3(nwg), dim3(8 * 16), 0, hs, a);
+    } else {
+      if (wide) hipLaunchKernelGGL((combine_kernel<32, 4, 4>), dim3(nwg * 4), dim3(32 * 8), 0, hs, a);
+      else hipLaunchKernelGGL((combine_kernel<8, 4, 1>), dim3(nwg), dim3(8 * 32), 0, hs, a);
+    }
   }
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
