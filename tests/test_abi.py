@@ -117,6 +117,25 @@ def test_workspace_closed_form():
     assert n == o + ml + cho + chml + dirs
 
 
+def test_workspace_closed_form_verify_rows():
+    # a 5-row verify sequence at G = 6 runs as decode sub-rows of 16 // 6 = 2
+    # rows (2, 2, 1: contexts prefix + 2, + 4, + 5), so a partial holds
+    # 2 * 6 = 12 (row, head) slots; 17 rows are the shortest prefill chunk
+    lay = mab.make_layout(24, 4, 128, 256, 1000)
+    b = _HostBatch([0, 5, 6, 23], [300, 1000, 50], max_pages=400)
+    n = _ws(lay, b)
+    wgs, rng, pmax = _decode_plan([302, 304, 305, 1001], 4)
+    tiles, f, h, rows = _chunk_plan(17, 4, 6)
+    slots = wgs * pmax
+    align = lambda x: -(-x // 256) * 256
+    o = align(slots * 12 * 128 * 4)
+    ml = align(slots * 12 * 8)
+    cho = align(tiles * f * h * rows * 128 * 4) if f > 1 else 0
+    chml = align(tiles * f * h * rows * 8) if f > 1 else 0
+    dirs = align(4 * 4 * 16)
+    assert n == o + ml + cho + chml + dirs
+
+
 def test_workspace_large_batch_holds_tables():
     """Batches beyond the kernel-argument tables (96 decode / 16 chunk
     sequences) keep the launch-order tables in the workspace."""
