@@ -4,17 +4,19 @@
 //   section 1  -- chunk rows and decode rows share one ForwardBatch and one
 //                 attention kernel (one launch serves both row kinds here);
 //   section 2  -- KV modes table: 32-value blocks with one fp16 scale, 34 bytes
-//                 (8-bit codes) or 18 bytes (4-bit codes), bit-exact codec.
+//                 (8-bit codes) or 18 bytes (4-bit codes), bit-exact codec; the
+//                 table's fp16 row is the unquantized 64-byte format.
 //
 // Kernels:
 //   append_kernel           -- encode new K/V rows into blocks at their page slots.
 //   mixed_attention_kernel  -- one launch over a flat list of work items: chunk
-//                              tiles first (heavy), then decode splits.
-//   decode_attention_kernel -- the same decode splits for batches without a chunk.
-// Decode splits stream raw blocks per wave and build 16x16x32 MFMA operands from
-// the bytes; chunk tiles dequantize each 32-key step once into a shared LDS tile
-// and run 32x32x16 MFMAs.  Keys always enter the MFMA as exact integer codes with
-// their block scale applied in fp32.
+//                              tiles first (heavy), then the decode stream.
+//   decode_attention_kernel -- the decode stream for batches without a chunk.
+//   combine_kernel, chunk_combine_kernel -- log-sum-exp merges of split ranges.
+// Decode waves stream raw blocks and build 16x16x32 MFMA operands from the
+// bytes; chunk tiles dequantize each 32-key step once into a shared LDS tile
+// and run 16x16x32 MFMAs.  Quantized keys enter the MFMA as exact integer codes
+// with their block scale applied in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,7 +32,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // plain 16-byte vector (not HIP's uint4 struct)
 
 // Loads through global-address-space pointers.  Every buffer the kernels
@@ -52,7 +53,7 @@ constexpr int kMaxVerify = 16;      // sequences with at most this many rows run
 constexpr int kMaxSeqs = 4096;
 constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this many stages per wave
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.f;  // chunk rows keep a stale max until it is 2^8 behind
+constexpr float kRescaleSlack = 8.f;  // a row keeps a stale max until it is 2^8 behind
 constexpr float kDecodeMaxFloor = -1e30f;  // initial running max of a decode slot (log2 units)
 
 template <int F> struct Fmt;
@@ -70,6 +71,8 @@ __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a 
 // rows of one query head: H heads of the group (the largest of 4, 2, 1 that
 // divides G) times 256/H rows.  Its K/V steps are dequantized once for all.
 __host__ __device__ inline int chunk_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+__host__ __device__ inline int chunk_rows(int group) { return 32 * kMixedWaves / chunk_heads(group); }
+
 // Rows of a sequence with q_len <= kMaxVerify (decode rows and short verify
 // rows) run on the decode path, in sub-rows of at most dec_tokens(G)
 // consecutive rows whose (row, head) pairs fill the 16 MFMA slots of a decode
@@ -80,12 +83,11 @@ __host__ __device__ inline int dec_tokens(int group) { return 16 / group; }
 __host__ __device__ inline int dec_subrows(int q_len, int group) {
   return (q_len + dec_tokens(group) - 1) / dec_tokens(group);
 }
-__host__ __device__ inline int chunk_rows(int group) { return 32 * kMixedWaves / chunk_heads(group); }
 
-// A sequence with more than one row is a chunk: ceil(q_len/rows) row tiles x
-// Hkv x G/H head groups, each cut into a number of key splits (one work item
-// per split).  A one-row sequence is a decode row: Hkv segments of
-// ceil(ctx/32) stages each in the decode stream.
+// A prefill chunk: ceil(q_len/rows) row tiles x Hkv x G/H head groups, each
+// cut into a number of key splits (one work item per split).  A decode
+// sub-row: Hkv segments of ceil(ctx/32) stages each in the decode stream, ctx
+// the keys its last row sees.
 __host__ __device__ inline int chunk_tiles(int q_len, int hkv, int group) {
   return ceil_div(q_len, chunk_rows(group)) * hkv * (group / chunk_heads(group));
 }
@@ -131,12 +133,12 @@ struct WsLayout {
   int64_t o_off, ml_off, cho_off, chml_off, dir_off, tab_off, total;
 };
 
-__host__ __device__ inline WsLayout ws_layout(int64_t n_slots, int group, int head_dim, int64_t n_chunk_rows,
+__host__ __device__ inline WsLayout ws_layout(int64_t n_slots, int per_slot, int head_dim, int64_t n_chunk_rows,
                                               int64_t n_dec_segs, int64_t tab_ints) {
-  WsLayout w;
+  WsLayout w;  // per_slot: (row, head) pairs of a decode partial
   w.o_off = 0;
-  w.ml_off = align256(w.o_off + n_slots * group * head_dim * 4);
-  w.cho_off = align256(w.ml_off + n_slots * group * 8);
+  w.ml_off = align256(w.o_off + n_slots * per_slot * head_dim * 4);
+  w.cho_off = align256(w.ml_off + n_slots * per_slot * 8);
   w.chml_off = align256(w.cho_off + n_chunk_rows * head_dim * 4);
   w.dir_off = align256(w.chml_off + n_chunk_rows * 8);
   w.tab_off = align256(w.dir_off + n_dec_segs * (int64_t)sizeof(DirEntry));
@@ -245,9 +247,10 @@ struct ItemCtx {
   int hkv, g, page_size;
 };
 
-// Online-softmax state of one decode wave.  The 16 MFMA slots are the G query
-// heads of the KV head; lane l serves slot l%16, and the four lanes of a slot
-// hold different keys of S^T and different dims of O^T.
+// Online-softmax state of one decode wave.  The 16 MFMA slots are the (row,
+// head) pairs of a decode sub-row (for a decode row, the G query heads of the
+// KV head); lane l serves slot l%16, and the four lanes of a slot hold
+// different keys of S^T and different dims of O^T.
 template <int NB>
 struct Group {
   half8_t q[NB];          // Q^T operand: slot l%16, dims 32b + 8(l/16) + [0,8)
