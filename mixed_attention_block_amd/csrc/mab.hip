@@ -375,21 +375,37 @@ __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
 }
 
 // Codes of value index dv (within block) for two keys at byte offsets o0, o1 of
-// their block payloads, as an fp16 pair of exact integers offset by
-// VBias<F>::kBias (1152 + code, or 1032 + code for 4-bit codes).
+// their 8-bit block payloads, as an fp16 pair of exact integers offset by
+// VBias<MAB_KV_Q8>::kBias (1152 + code).
+__device__ inline half2_t lds_code_pair_q8_biased(const uint8_t* base, int o0, int o1, int dv) {
+  const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
+  return __builtin_bit_cast(half2_t, w ^ 0x64806480u);
+}
+
+// V operand rows of a block's two 16-row tiles.  8-bit codes: row n of tile t2
+// is value 16*t2 + n, one byte read per key and value.  4-bit codes and fp16
+// values: row n of tile t2 is value 2n + t2, one read per key serving both
+// tiles (measured: faster for those two, slower for 8-bit codes, where the
+// paired layout's live registers spill).
+template <int F> constexpr bool kPairedV = F != MAB_KV_Q8;
+
+// Values 2v and 2v+1 (within block) of two keys whose block payloads start at
+// byte offsets o0, o1: p0 = (value 2v of key 0, of key 1), p1 = (value 2v+1 of
+// each), as fp16 pairs of exact integers offset by VBias<MAB_KV_Q4>::kBias
+// (1032 + code), or the fp16 values themselves.  The two values of a key sit
+// in one byte (4-bit codes) or one 4-byte word (fp16), so one read per key
+// serves both.
 template <int F>
-__device__ inline half2_t lds_code_pair_biased(const uint8_t* base, int o0, int o1, int dv) {
-  if constexpr (F == MAB_KV_F16) {  // fp16 values: value dv of each key
-    const uint32_t w = (uint32_t)*reinterpret_cast<const uint16_t*>(base + o0 + 2 * dv) |
-                       ((uint32_t)*reinterpret_cast<const uint16_t*>(base + o1 + 2 * dv) << 16);
-    return __builtin_bit_cast(half2_t, w);
-  } else if constexpr (F == MAB_KV_Q8) {
-    const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
-    return __builtin_bit_cast(half2_t, w ^ 0x64806480u);
-  } else {
-    uint32_t w = (uint32_t)base[o0 + (dv >> 1)] | ((uint32_t)base[o1 + (dv >> 1)] << 16);
-    w = ((dv & 1) ? (w >> 4) : w) & 0x000F000Fu;
-    return __builtin_bit_cast(half2_t, w ^ 0x64086408u);
+__device__ inline void lds_value_pairs_biased(const uint8_t* base, int o0, int o1, int v, half2_t& p0, half2_t& p1) {
+  if constexpr (F == MAB_KV_F16) {
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(base + o0 + 4 * v);
+    const uint32_t b = *reinterpret_cast<const uint32_t*>(base + o1 + 4 * v);
+    p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x05040100u));
+    p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x07060302u));
+  } else {  // 4-bit codes: value 2v in the low nibble of byte v, 2v+1 in the high nibble
+    const uint32_t w = (uint32_t)base[o0 + v] | ((uint32_t)base[o1 + v] << 16);
+    p0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u);
+    p1 = __builtin_bit_cast(half2_t, ((w >> 4) & 0x000F000Fu) ^ 0x64086408u);
   }
 }
 
@@ -577,25 +593,45 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
       const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
       gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
     }
+    if constexpr (!kPairedV<VF>) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int dv = 16 * t2 + n;  // value index inside block b
-      half2_t vp[4];
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int dv = 16 * t2 + n;  // value index inside block b
+        half2_t vq[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
-        vp[e] = lds_code_pair_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
-                                         (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, dv);
-        if constexpr (VF == MAB_KV_F16) {
-          // f16 values of keys past the range are whatever the pool holds
-          // there (possibly NaN): zero them, as their weight is zero
-          if (tail) {
-            if (kbase + ka >= kend) vp[e][0] = (half_t)0.f;
-            if (kbase + ka + 1 >= kend) vp[e][1] = (half_t)0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
+          vq[e] = lds_code_pair_q8_biased(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
+                                          (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, dv);
+        }
+        const half8_t vc = half8_t{vq[0][0], vq[0][1], vq[1][0], vq[1][1], vq[2][0], vq[2][1], vq[3][0], vq[3][1]};
+        gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
+      }
+      continue;
+    }
+    // the block's two V^T tiles: row n of tile t2 is value 2n + t2 of the block
+    half2_t vp[2][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
+      lds_value_pairs_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
+                                 (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, n, vp[0][e], vp[1][e]);
+      if constexpr (VF == MAB_KV_F16) {
+        // f16 values of keys past the range are whatever the pool holds there
+        // (possibly NaN): zero them, as their weight is zero
+        if (tail) {
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            if (kbase + ka >= kend) vp[t2][e][0] = (half_t)0.f;
+            if (kbase + ka + 1 >= kend) vp[t2][e][1] = (half_t)0.f;
           }
         }
       }
-      const half8_t vc = half8_t{vp[0][0], vp[0][1], vp[1][0], vp[1][1], vp[2][0], vp[2][1], vp[3][0], vp[3][1]};
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const half8_t vc = half8_t{vp[t2][0][0], vp[t2][0][1], vp[t2][1][0], vp[t2][1][1],
+                                 vp[t2][2][0], vp[t2][2][1], vp[t2][3][0], vp[t2][3][1]};
       gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
     }
   }
@@ -1058,19 +1094,26 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
   }
-  // lane (n, j) holds dims 16t + 4j + [0,4) of slot n
-  if (whole) {
-    float* dst = a.out + orow * D + 4 * j;
-    const float inv = 1.f / lsum;
+  const float inv = whole ? 1.f / lsum : 1.f;
+  const int64_t pi = slot * a.dec_slots + n;
+  float* dst = whole ? a.out + orow * D : a.o_part + pi * D;
+  if constexpr (!kPairedV<VF>) {
+    // lane (n, j) holds dims 16t + 4j + [0,4) of slot n
 #pragma unroll
-    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t] * inv;
+    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t + 4 * j) = gr.o[t] * inv;
   } else {
-    const int64_t pi = slot * a.dec_slots + n;
-    float* dst = a.o_part + pi * D + 4 * j;
+    // lane (n, j) holds rows 4j + [0,4) of the block's two tiles, i.e. values
+    // 8j + 2r + t2 (o[2b + t2][r]) of block b: eight consecutive dims of slot n
 #pragma unroll
-    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t) = gr.o[t];
-    if (j == 0) a.ml_part[pi] = make_float2(gr.m, lsum);
+    for (int b = 0; b < NB; ++b) {
+      const float4_t* ob = &gr.o[2 * b];
+      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j) =
+          float4_t{ob[0][0], ob[1][0], ob[0][1], ob[1][1]} * inv;
+      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j + 4) =
+          float4_t{ob[0][2], ob[1][2], ob[0][3], ob[1][3]} * inv;
+    }
   }
+  if (!whole && j == 0) a.ml_part[pi] = make_float2(gr.m, lsum);
 }
 
 // Decode worker w (one wave): stages [w*R, min((w+1)*R, units)) of the decode
