@@ -267,6 +267,12 @@ template <int F> struct VBias;
 template <> struct VBias<MAB_KV_Q8> { static constexpr float kBias = 1152.f; };
 template <> struct VBias<MAB_KV_Q4> { static constexpr float kBias = 1032.f; };
 template <> struct VBias<MAB_KV_F16> { static constexpr float kBias = 0.f; };  // the values themselves
+// Where the sums of the weights are kept: on the matrix cores (an MFMA against
+// ones, every row of vb[b] the slot's sum), or, for 8-bit K with 4-bit V, as
+// each lane's share in vb[b][0] (dot products on the vector unit, the slot's
+// four lanes added at the end), which frees the registers whose spill slowed
+// that mix by 9%; the other formats run faster on the matrix cores.
+template <int KF, int VF> constexpr bool kWeightSumsOnVALU = KF == MAB_KV_Q8 && VF == MAB_KV_Q4;
 
 template <int NB>
 __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
@@ -566,7 +572,10 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) gr.vb[b] *= alpha;
+    for (int b = 0; b < NB; ++b) {
+      if constexpr (kWeightSumsOnVALU<KF, VF>) gr.vb[b][0] *= alpha;
+      else gr.vb[b] *= alpha;
+    }
     gr.l *= alpha;
     gr.m = m_new;
   }
@@ -590,8 +599,16 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
     const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     if constexpr (VBias<VF>::kBias != 0.f) {
-      const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-      gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
+      if constexpr (kWeightSumsOnVALU<KF, VF>) {
+        const half2_t one2 = half2_t{1.f, 1.f};
+        float acc = gr.vb[b][0];  // this lane's eight weights of the block
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(half2_t{pf[2 * e], pf[2 * e + 1]}, one2, acc, false);
+        gr.vb[b][0] = acc;
+      } else {
+        const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
+      }
     }
     if constexpr (!kPairedV<VF>) {
 #pragma unroll
@@ -1086,13 +1103,22 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+  float vbt[NB];  // the slot's sum of each block's weights
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    vbt[b] = gr.vb[b][0];
+    if constexpr (VBias<VF>::kBias != 0.f && kWeightSumsOnVALU<KF, VF>) {  // add the slot's four lanes
+      vbt[b] += __shfl_xor(vbt[b], 16);
+      vbt[b] += __shfl_xor(vbt[b], 32);
+    }
+  }
   if (!live) return;
   // remove the code bias: o -= bias * (sum of the block's weights)
   if constexpr (VBias<VF>::kBias != 0.f) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
+      for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * vbt[b];
   }
   const float inv = whole ? 1.f / lsum : 1.f;
   const int64_t pi = slot * a.dec_slots + n;
