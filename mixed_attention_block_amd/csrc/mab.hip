@@ -52,6 +52,11 @@ constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr int kMaxVerify = 16;      // sequences with at most this many rows run on the decode path
 constexpr int kMaxSeqs = 4096;
 constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this many stages per wave
+// Stages a decode wave has in flight beyond the one it computes on.  One is
+// faster than two for every format (decode16 q8: 70.6 -> 61.4 us): the second
+// register set of 16-byte loads crowds out the compute state at two waves per
+// SIMD.
+constexpr int kDecodeDepth = 1;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // a row keeps a stale max until it is 2^8 behind
 constexpr float kDecodeMaxFloor = -1e30f;  // initial running max of a decode slot (log2 units)
@@ -254,7 +259,8 @@ struct ItemCtx {
 template <int NB>
 struct Group {
   half8_t q[NB];          // Q^T operand: slot l%16, dims 32b + 8(l/16) + [0,8)
-  float4_t o[2 * NB];     // O^T: slot l%16, dims 16t + 4(l/16) + [0,4), V codes taken with their bias
+  float4_t o[2 * NB];     // O^T tile t of block t/2: slot l%16, rows 4(l/16) + [0,4), row r being value
+                          // 2r + t%2 of the block; V codes taken with their bias
   float4_t vb[NB];        // per block: sum over keys of the P * V-scale weights (the bias correction of o)
   float m, l;             // running max (log2 units) and lane-partial sum
   int limit;              // last key position visible to the slot (-1: none)
@@ -267,12 +273,7 @@ template <int F> struct VBias;
 template <> struct VBias<MAB_KV_Q8> { static constexpr float kBias = 1152.f; };
 template <> struct VBias<MAB_KV_Q4> { static constexpr float kBias = 1032.f; };
 template <> struct VBias<MAB_KV_F16> { static constexpr float kBias = 0.f; };  // the values themselves
-// Where the sums of the weights are kept: on the matrix cores (an MFMA against
-// ones, every row of vb[b] the slot's sum), or, for 8-bit K with 4-bit V, as
-// each lane's share in vb[b][0] (dot products on the vector unit, the slot's
-// four lanes added at the end), which frees the registers whose spill slowed
-// that mix by 9%; the other formats run faster on the matrix cores.
-template <int KF, int VF> constexpr bool kWeightSumsOnVALU = KF == MAB_KV_Q8 && VF == MAB_KV_Q4;
+
 
 template <int NB>
 __device__ inline void group_init(Group<NB>& gr, const half_t* qrow, int limit, int lane) {
@@ -380,27 +381,13 @@ __device__ inline half8_t lds_codes8_q4(const uint8_t* base, int off) {
   return codes8_q4(__builtin_amdgcn_alignbyte(d1, d0, sh));
 }
 
-// Codes of value index dv (within block) for two keys at byte offsets o0, o1 of
-// their 8-bit block payloads, as an fp16 pair of exact integers offset by
-// VBias<MAB_KV_Q8>::kBias (1152 + code).
-__device__ inline half2_t lds_code_pair_q8_biased(const uint8_t* base, int o0, int o1, int dv) {
-  const uint32_t w = (uint32_t)base[o0 + dv] | ((uint32_t)base[o1 + dv] << 16);
-  return __builtin_bit_cast(half2_t, w ^ 0x64806480u);
-}
-
-// V operand rows of a block's two 16-row tiles.  8-bit codes: row n of tile t2
-// is value 16*t2 + n, one byte read per key and value.  4-bit codes and fp16
-// values: row n of tile t2 is value 2n + t2, one read per key serving both
-// tiles (measured: faster for those two, slower for 8-bit codes, where the
-// paired layout's live registers spill).
-template <int F> constexpr bool kPairedV = F != MAB_KV_Q8;
-
 // Values 2v and 2v+1 (within block) of two keys whose block payloads start at
 // byte offsets o0, o1: p0 = (value 2v of key 0, of key 1), p1 = (value 2v+1 of
-// each), as fp16 pairs of exact integers offset by VBias<MAB_KV_Q4>::kBias
-// (1032 + code), or the fp16 values themselves.  The two values of a key sit
-// in one byte (4-bit codes) or one 4-byte word (fp16), so one read per key
-// serves both.
+// each), as fp16 pairs of exact integers offset by VBias<F>::kBias (1152 +
+// code, or 1032 + code for 4-bit codes), or the fp16 values themselves.  The
+// two values of a key sit in one 2-byte word (8-bit codes), one byte (4-bit
+// codes) or one 4-byte word (fp16), so one read per key serves both.  Row n
+// of a block's two 16-row V^T tiles t2 is value 2n + t2.
 template <int F>
 __device__ inline void lds_value_pairs_biased(const uint8_t* base, int o0, int o1, int v, half2_t& p0, half2_t& p1) {
   if constexpr (F == MAB_KV_F16) {
@@ -408,6 +395,12 @@ __device__ inline void lds_value_pairs_biased(const uint8_t* base, int o0, int o
     const uint32_t b = *reinterpret_cast<const uint32_t*>(base + o1 + 4 * v);
     p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x05040100u));
     p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x07060302u));
+  } else if constexpr (F == MAB_KV_Q8) {
+    uint32_t w = (uint32_t)*reinterpret_cast<const uint16_t*>(base + o0 + 2 * v) |
+                 ((uint32_t)*reinterpret_cast<const uint16_t*>(base + o1 + 2 * v) << 16);
+    w ^= 0x80808080u;  // bytes: key 0 value 2v, 2v+1, key 1 value 2v, 2v+1; 0x64xx is 1152 + code
+    p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w, 0x04020400u));
+    p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w, 0x04030401u));
   } else {  // 4-bit codes: value 2v in the low nibble of byte v, 2v+1 in the high nibble
     const uint32_t w = (uint32_t)base[o0 + v] | ((uint32_t)base[o1 + v] << 16);
     p0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u);
@@ -572,10 +565,7 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 #pragma unroll
     for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if constexpr (kWeightSumsOnVALU<KF, VF>) gr.vb[b][0] *= alpha;
-      else gr.vb[b] *= alpha;
-    }
+    for (int b = 0; b < NB; ++b) gr.vb[b] *= alpha;
     gr.l *= alpha;
     gr.m = m_new;
   }
@@ -599,32 +589,8 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
     const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     if constexpr (VBias<VF>::kBias != 0.f) {
-      if constexpr (kWeightSumsOnVALU<KF, VF>) {
-        const half2_t one2 = half2_t{1.f, 1.f};
-        float acc = gr.vb[b][0];  // this lane's eight weights of the block
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(half2_t{pf[2 * e], pf[2 * e + 1]}, one2, acc, false);
-        gr.vb[b][0] = acc;
-      } else {
-        const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-        gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
-      }
-    }
-    if constexpr (!kPairedV<VF>) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int dv = 16 * t2 + n;  // value index inside block b
-        half2_t vq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
-          vq[e] = lds_code_pair_q8_biased(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
-                                          (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, dv);
-        }
-        const half8_t vc = half8_t{vq[0][0], vq[0][1], vq[1][0], vq[1][1], vq[2][0], vq[2][1], vq[3][0], vq[3][1]};
-        gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
-      }
-      continue;
+      const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
     }
     // the block's two V^T tiles: row n of tile t2 is value 2n + t2 of the block
     half2_t vp[2][4];
@@ -1103,41 +1069,24 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   float lsum = gr.l;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  float vbt[NB];  // the slot's sum of each block's weights
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    vbt[b] = gr.vb[b][0];
-    if constexpr (VBias<VF>::kBias != 0.f && kWeightSumsOnVALU<KF, VF>) {  // add the slot's four lanes
-      vbt[b] += __shfl_xor(vbt[b], 16);
-      vbt[b] += __shfl_xor(vbt[b], 32);
-    }
-  }
   if (!live) return;
   // remove the code bias: o -= bias * (sum of the block's weights)
   if constexpr (VBias<VF>::kBias != 0.f) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * vbt[b];
+      for (int t2 = 0; t2 < 2; ++t2) gr.o[2 * b + t2] -= VBias<VF>::kBias * gr.vb[b][0];
   }
   const float inv = whole ? 1.f / lsum : 1.f;
   const int64_t pi = slot * a.dec_slots + n;
   float* dst = whole ? a.out + orow * D : a.o_part + pi * D;
-  if constexpr (!kPairedV<VF>) {
-    // lane (n, j) holds dims 16t + 4j + [0,4) of slot n
+  // lane (n, j) holds rows 4j + [0,4) of each block's two tiles, i.e. values
+  // 8j + 2r + t2 (o[2b + t2][r]) of block b: eight consecutive dims of slot n
 #pragma unroll
-    for (int t = 0; t < 2 * NB; ++t) *reinterpret_cast<float4_t*>(dst + 16 * t + 4 * j) = gr.o[t] * inv;
-  } else {
-    // lane (n, j) holds rows 4j + [0,4) of the block's two tiles, i.e. values
-    // 8j + 2r + t2 (o[2b + t2][r]) of block b: eight consecutive dims of slot n
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float4_t* ob = &gr.o[2 * b];
-      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j) =
-          float4_t{ob[0][0], ob[1][0], ob[0][1], ob[1][1]} * inv;
-      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j + 4) =
-          float4_t{ob[0][2], ob[1][2], ob[0][3], ob[1][3]} * inv;
-    }
+  for (int b = 0; b < NB; ++b) {
+    const float4_t* ob = &gr.o[2 * b];
+    *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j) = float4_t{ob[0][0], ob[1][0], ob[0][1], ob[1][1]} * inv;
+    *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j + 4) = float4_t{ob[0][2], ob[1][2], ob[0][3], ob[1][3]} * inv;
   }
   if (!whole && j == 0) a.ml_part[pi] = make_float2(gr.m, lsum);
 }
@@ -1401,9 +1350,8 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
   }
   constexpr int nw = HAS_CHUNK ? kMixedWaves : kDecodeWaves;
   const int wave = threadIdx.x >> 6;
-  // f16 stages are 16 KB (twice q8): one stage in flight instead of two
-  decode_worker<NB, KF, VF, KF == MAB_KV_F16 ? 1 : 2>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
-                                                      (b - a.n_chunk_items) * nw + wave);
+  decode_worker<NB, KF, VF, kDecodeDepth>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
+                                         (b - a.n_chunk_items) * nw + wave);
 }
 
 template <int NB, int KF, int VF>
