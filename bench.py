@@ -238,8 +238,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; runs on more than one GPU are not "
-              "part of it (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU; runs on more than one GPU are not supported (the path "
+              "shards by KV head, sequence or key range without kernel changes).", file=sys.stderr)
         sys.exit(2)
 
     import torch
