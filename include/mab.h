@@ -180,6 +180,23 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
 /* Static English text for a status code (never NULL). */
 const char* mab_status_string(int32_t status);
 
+/* mab_debug_status: the device-side check of page ids (the block table's
+ * values, which the host cannot see).
+ *
+ * With MAB_DEBUG=1 in the environment of the calling process (read at each
+ * kv_append_quant / mixed_attention_fwd call), every page id the kernels read
+ * from the block table is checked against [0, num_pages); an id outside it
+ * sets a flag on the current device and page 0 is read or written instead,
+ * so the kernels never leave the pools (the results of the affected rows are
+ * then meaningless).  Without MAB_DEBUG=1 page ids are trusted and an invalid
+ * one is undefined behaviour.
+ *
+ * Returns 1 if the flag is set, 0 if not, or -MAB_ERR_HIP if the device could
+ * not be read.  reset != 0 clears the flag after reading.  Synchronous: waits
+ * for all work on the current device first (every stream).  A debugging aid:
+ * the pages define no error reporting of their own. */
+int32_t mab_debug_status(int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

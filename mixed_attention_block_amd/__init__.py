@@ -66,6 +66,7 @@ def _lib():
         lib.mixed_attention_fwd.argtypes = [lay, bat, P, P, P, f32, P, P, i64, P]
         lib.mixed_attention_fwd.restype = i32
         lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
+        lib.mab_debug_status.argtypes, lib.mab_debug_status.restype = [i32], i32
         _lib_handle = lib
     return _lib_handle
 
@@ -162,3 +163,12 @@ def mixed_attention_fwd(layout, batch, q, k_pool, v_pool, sm_scale, out, workspa
 
 def mab_status_string(status):
     return _lib().mab_status_string(int(status)).decode()
+
+
+def mab_debug_status(reset=True):
+    """1 if a kernel met an out-of-range page id since the last reset (checked
+    only while MAB_DEBUG=1 is set in the environment), else 0."""
+    st = _lib().mab_debug_status(1 if reset else 0)
+    if st < 0:
+        raise MabError(-st, "mab_debug_status")
+    return st

@@ -19,6 +19,7 @@
 // with their block scale applied in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <vector>
@@ -44,6 +45,30 @@ __device__ inline u32x4_t gload16_nt(const void* p) {
   return __builtin_nontemporal_load((const MAB_GLOBAL u32x4_t*)p);
 }
 __device__ inline int32_t gload_i32(const int32_t* p) { return *(const MAB_GLOBAL int32_t*)p; }
+
+// Debug mode (MAB_DEBUG=1 in the environment of the calling process): every
+// page id read from the block table is checked against the pool; an id
+// outside [0, num_pages) sets g_mab_debug_flag and page 0 is read or written
+// instead, so the kernels stay inside the pools.  Otherwise ids are trusted.
+// The kernels take it as a template flag: separate instantiations, so the
+// normal ones carry no check.
+__device__ int g_mab_debug_flag;
+// The register form: an out-of-range id sets `bad`, which the caller reports
+// once, after its loop.
+__device__ inline int clamp_page(int page, int num_pages, int debug, int& bad) {
+  const int out = debug & ((unsigned)page >= (unsigned)num_pages);
+  bad |= out;
+  return out ? 0 : page;
+}
+__device__ inline void report_bad_page(int bad) {
+  if (bad) *(volatile int*)&g_mab_debug_flag = 1;
+}
+__device__ inline int checked_page(int page, int num_pages, int debug) {
+  int bad = 0;
+  page = clamp_page(page, num_pages, debug, bad);
+  report_bad_page(bad);
+  return page;
+}
 
 constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two work-groups per CU)
 constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
@@ -215,13 +240,13 @@ __device__ inline void encode_block(const half_t* __restrict__ x, uint8_t* __res
   }
 }
 
-template <int KF, int VF>
+template <int KF, int VF, bool DBG>
 __global__ void __launch_bounds__(256)
 append_kernel(const half_t* __restrict__ k_new, const half_t* __restrict__ v_new,
               uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
               const int32_t* __restrict__ q_start, const int32_t* __restrict__ prefix_len,
               const int32_t* __restrict__ block_table, int num_seqs, int num_rows,
-              int max_pages, int hkv, int head_dim, int page_size) {
+              int max_pages, int hkv, int head_dim, int page_size, int num_pages) {
   const int nb = head_dim / 32;
   const int64_t per_side = (int64_t)num_rows * hkv * nb;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -233,7 +258,7 @@ append_kernel(const half_t* __restrict__ k_new, const half_t* __restrict__ v_new
   const int row = (int)(u / ((int64_t)nb * hkv));
   const int s = find_seq(q_start, num_seqs, row);
   const int pos = prefix_len[s] + (row - q_start[s]);
-  const int page = block_table[(int64_t)s * max_pages + pos / page_size];
+  const int page = checked_page(block_table[(int64_t)s * max_pages + pos / page_size], num_pages, DBG);
   const int slot = pos % page_size;
   const int64_t tok = ((int64_t)page * hkv + g) * page_size + slot;
   const half_t* src = (is_v ? v_new : k_new) + ((int64_t)row * hkv + g) * head_dim + 32 * b;
@@ -947,6 +972,7 @@ struct AttnArgs {
   int tabs_in_ws;           // tables in the workspace (1) or in `tabs` (0)
   float c;                  // sm_scale * log2(e)
   ArgTabs tabs;
+  int num_pages;            // pages of each pool (page ids are checked against it in debug mode)
 };
 
 struct TabView {
@@ -1003,7 +1029,7 @@ __device__ inline void dec_init(Group<NB>& gr, const half_t* qrow, int limit, in
 // stages ahead, with loads that bypass the caches' retention (every byte is
 // read once), through the wave's own LDS stage buffer wbuf.  A whole segment
 // writes the output, a piece its partial at `slot`.
-template <int NB, int KF, int VF, int DEPTH>
+template <int NB, int KF, int VF, int DEPTH, bool DBG>
 __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int r0, int ntok, int ctx, int g,
                                     int kb, int ke, bool whole, int64_t slot) {
   constexpr int D = 32 * NB;
@@ -1021,7 +1047,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   // page ids of the piece's 16-key runs, 64 at a time (one per lane)
   auto page_window = [&](int win) {
     const int key = kb + 16 * (64 * win + lane);
-    return key < ke ? gload_i32(ic.bt_row + key / a.page_size) : 0;
+    return key < ke ? checked_page(gload_i32(ic.bt_row + key / a.page_size), a.num_pages, DBG) : 0;
   };
   int my_page = page_window(0);
   const int tn = n / G, hn = n % G;  // this lane's slot: row r0 + tn, head g*G + hn
@@ -1094,7 +1120,7 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
 // Decode worker w (one wave): stages [w*R, min((w+1)*R, units)) of the decode
 // stream, one piece per segment it touches.  The worker that runs a segment's
 // first stage records where the segment's results went.
-template <int NB, int KF, int VF, int DEPTH>
+template <int NB, int KF, int VF, int DEPTH, bool DBG>
 __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
   const int x0 = w * a.dec_range, x1 = min(x0 + a.dec_range, a.dec_units);
   if (x0 >= x1) return;
@@ -1111,7 +1137,7 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
     const int r0 = tv.dec_r0[e];
     const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
     const int64_t slot = (int64_t)w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF, DEPTH>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
+    decode_piece<NB, KF, VF, DEPTH, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
                                     min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
     if (first && (threadIdx.x & 63) == 0) {
       DirEntry d;
@@ -1131,8 +1157,10 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
 // group hp (H heads), keys [kb, ke) of the rows' visible range.  Wave (hh, rg)
 // serves query head hp*H + hh of the group and rows 32*rg .. 32*rg+31 of the
 // tile.  pslot < 0: the item covers every key of its rows and writes the
-// output; otherwise its partial goes to slot pslot.
-template <int NB, int KF, int VF>
+// output; otherwise its partial goes to slot pslot.  DBG: check page ids
+// (debug mode; a separate instantiation keeps the checks out of the normal
+// step loop).
+template <int NB, int KF, int VF, bool DBG>
 __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
                                   int g, int hp, int qt, int kb, int ke, int64_t pslot) {
   // every argument is the same across the work-group; say so, so that the
@@ -1196,7 +1224,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   // the block table is read-only during the call: scalar loads
   const __attribute__((address_space(4))) int32_t* bt_const =
       (const __attribute__((address_space(4))) int32_t*)(wave_uniform(ic.bt_row));
-  int u_pg = 0, u_pg_next = 0;
+  int u_pg = 0, u_pg_next = 0, bad_page = 0;
   auto issue_uniform = [&]() {
     const uint8_t* base = pool + (((int64_t)u_pg * ic.hkv + g) * ps + u_r) * rec;
     if (u_is_v) chunk_raw_load_al<VF>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
@@ -1206,7 +1234,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
       u_r = 0;
       ++u_q;
       u_pg = u_pg_next;
-      u_pg_next = u_q < q_last ? bt_const[u_q + 1] : 0;
+      u_pg_next = u_q < q_last ? clamp_page(bt_const[u_q + 1], a.num_pages, DBG, bad_page) : 0;
     }
   };
   // per-lane walk: position of a step's first key (page index q, slot r),
@@ -1237,7 +1265,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   int pidx, next_slot = 0, pg_next = 0;
   auto fetch_page = [&](int st) {
     lane_page_slot(p_page, st, pidx, next_slot);
-    pg_next = ic.bt_row[pidx];
+    pg_next = clamp_page(ic.bt_row[pidx], a.num_pages, DBG, bad_page);
     p_page = advance(p_page);
   };
   auto issue = [&](int st) {  // loads of step st (issued in step order)
@@ -1251,8 +1279,8 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   };
   if (has_unit && nst > 0) {
     if (uniform) {
-      u_pg = bt_const[u_q];
-      u_pg_next = u_q < q_last ? bt_const[u_q + 1] : 0;
+      u_pg = clamp_page(bt_const[u_q], a.num_pages, DBG, bad_page);
+      u_pg_next = u_q < q_last ? clamp_page(bt_const[u_q + 1], a.num_pages, DBG, bad_page) : 0;
     } else {
       fetch_page(0);
     }
@@ -1272,6 +1300,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, a.c, lane);
     __syncthreads();
   }
+  report_bad_page(bad_page);
   if (nrows == 0) return;
   const int n = lane & 15, j = lane >> 4;
 #pragma unroll
@@ -1307,7 +1336,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
 // head g and head group hp, key split (local % F) of F = ch_split[c].  The visible keys of
 // the tile's rows, [0, prefix + last row + 1), are cut into F ranges of whole
 // steps.
-template <int NB, int KF, int VF>
+template <int NB, int KF, int VF, bool DBG>
 __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   const TabView tv = tab_view(a);
   const int c = wave_find(tv.ch_item, a.n_chunk, item);
@@ -1326,31 +1355,31 @@ __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   ic.page_size = a.page_size;
   const int tile_end = prefix + min(q_len, (qt + 1) * R);  // keys past the tile's last row are never seen
   if (F == 1) {
-    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
+    chunk_item<NB, KF, VF, DBG>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
     return;
   }
   const int len = ceil_div(ceil_div(tile_end, F), kStepKeys) * kStepKeys;
   const int kb = min(j * len, tile_end), ke = min(kb + len, tile_end);
   if (kb < ke) {
-    chunk_item<NB, KF, VF>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
+    chunk_item<NB, KF, VF, DBG>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
   } else {  // an empty split: a neutral partial (no keys) for every row of the tile
     const int64_t base = (int64_t)item * H * R;
     for (int u = threadIdx.x; u < H * R; u += blockDim.x) a.ch_ml[base + u] = make_float2(-INFINITY, 0.f);
   }
 }
 
-template <int NB, int KF, int VF, bool HAS_CHUNK>
+template <int NB, int KF, int VF, bool HAS_CHUNK, bool DBG>
 __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
   const int b = blockIdx.x;
   if constexpr (HAS_CHUNK) {
     if (b < a.n_chunk_items) {
-      chunk_work<NB, KF, VF>(a, smem, b);
+      chunk_work<NB, KF, VF, DBG>(a, smem, b);
       return;
     }
   }
   constexpr int nw = HAS_CHUNK ? kMixedWaves : kDecodeWaves;
   const int wave = threadIdx.x >> 6;
-  decode_worker<NB, KF, VF, kDecodeDepth>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
+  decode_worker<NB, KF, VF, kDecodeDepth, DBG>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
                                          (b - a.n_chunk_items) * nw + wave);
 }
 
@@ -1369,20 +1398,20 @@ constexpr int mixed_smem_bytes() {
 // Batches with a chunk: chunk tiles and decode stream ranges in one launch of
 // kMixedWaves-wave work-groups, two waves per SIMD (one work-group per
 // compute unit).
-template <int NB, int KF, int VF>
+template <int NB, int KF, int VF, bool DBG>
 __global__ void __launch_bounds__(64 * kMixedWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 mixed_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
-  attention_body<NB, KF, VF, true>(a, smem);
+  attention_body<NB, KF, VF, true, DBG>(a, smem);
 }
 
 // Decode-only batches: kDecodeWaves waves per work-group, two per SIMD (room
 // for two stages in flight per wave).
-template <int NB, int KF, int VF>
+template <int NB, int KF, int VF, bool DBG>
 __global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 decode_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF>(kDecodeWaves)];
-  attention_body<NB, KF, VF, false>(a, smem);
+  attention_body<NB, KF, VF, false, DBG>(a, smem);
 }
 
 // Merges the pieces of decode segments that span several decode workers.
@@ -1606,6 +1635,11 @@ struct HostPlan {
   int64_t n_slots = 0;
 };
 
+int debug_mode() {
+  const char* e = getenv("MAB_DEBUG");
+  return e && e[0] == '1' ? 1 : 0;
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -1735,27 +1769,35 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
                    void* vp, hipStream_t st) {
   const int64_t n = 2LL * B->num_rows * L->num_kv_heads * (L->head_dim / 32);
   const int grid = (int)((n + 255) / 256);
-  hipLaunchKernelGGL((append_kernel<KF, VF>), dim3(grid), dim3(256), 0, st, (const half_t*)kn,
-                     (const half_t*)vn, (uint8_t*)kp, (uint8_t*)vp, B->q_start, B->prefix_len,
-                     B->block_table, B->num_seqs, B->num_rows, B->max_pages_per_seq, L->num_kv_heads,
-                     L->head_dim, L->page_size);
+  auto kernel = debug_mode() ? append_kernel<KF, VF, true> : append_kernel<KF, VF, false>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, (const half_t*)kn, (const half_t*)vn, (uint8_t*)kp,
+                     (uint8_t*)vp, B->q_start, B->prefix_len, B->block_table, B->num_seqs, B->num_rows,
+                     B->max_pages_per_seq, L->num_kv_heads, L->head_dim, L->page_size, L->num_pages);
 }
 
-template <int NB, int KF, int VF>
-void launch_attention(const AttnArgs& a, int grid, hipStream_t st) {
+template <int NB, int KF, int VF, bool DBG>
+void launch_attention_dbg(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kMixedWaves), 0, st, a);
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF, DBG>), dim3(grid), dim3(64 * kMixedWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
+    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF, DBG>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
+}
+
+// Debug mode takes instantiations of their own: the page-id checks stay out
+// of the normal kernels' code.
+template <int NB, int KF, int VF>
+void launch_attention(const AttnArgs& a, int grid, hipStream_t st, bool debug) {
+  if (debug) launch_attention_dbg<NB, KF, VF, true>(a, grid, st);
+  else launch_attention_dbg<NB, KF, VF, false>(a, grid, st);
 }
 
 template <int NB>
-void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st) {
-  if (L->k_format == MAB_KV_F16) launch_attention<NB, MAB_KV_F16, MAB_KV_F16>(a, grid, st);
-  else if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st);
-  else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st);
-  else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st);
-  else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st);
+void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st, bool dbg) {
+  if (L->k_format == MAB_KV_F16) launch_attention<NB, MAB_KV_F16, MAB_KV_F16>(a, grid, st, dbg);
+  else if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st, dbg);
+  else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st, dbg);
+  else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st, dbg);
+  else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st, dbg);
 }
 
 }  // namespace
@@ -1845,6 +1887,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   a.dec_units = hp.dec_units;
   a.dec_range = hp.dec_range;
   a.dec_pmax = hp.dec_pmax;
+  a.num_pages = layout->num_pages;
   a.dec_slots = hp.dec_slots;
   a.c = sm_scale * kLog2e;
   a.tabs_in_ws = hp.n_dec > kArgDec || hp.n_chunk > kArgChunk;
@@ -1856,8 +1899,9 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
     fill_arg_tabs(layout, batch, &a);
   }
   const int grid = hp.n_chunk_items + hp.dec_wgs;
-  if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs);
-  else launch_attention_nb<4>(layout, a, grid, hs);
+  const bool dbg = debug_mode();
+  if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs, dbg);
+  else launch_attention_nb<4>(layout, a, grid, hs, dbg);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   if (hp.ch_splits) {
     hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * chunk_combine_parts(layout->head_dim)),
@@ -1876,6 +1920,17 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
     }
   }
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
+}
+
+int32_t mab_debug_status(int32_t reset) {
+  int flag = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return -MAB_ERR_HIP;
+  if (hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_mab_debug_flag), sizeof(flag)) != hipSuccess) return -MAB_ERR_HIP;
+  if (reset) {
+    const int zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_mab_debug_flag), &zero, sizeof(zero)) != hipSuccess) return -MAB_ERR_HIP;
+  }
+  return flag;
 }
 
 const char* mab_status_string(int32_t status) {

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"kv_append_quant", "mixed_attention_fwd", "attention_workspace_bytes",
-            "kv_pool_bytes", "kv_block_bytes", "mab_status_string"} <= set(names)
+            "kv_pool_bytes", "kv_block_bytes", "mab_status_string", "mab_debug_status"} <= set(names)
     lib = ctypes.CDLL(mab.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
