@@ -16,6 +16,10 @@ Everything here is plain, slow and written to be checked by eye:
                     and gathering them back by logical position.
 * ``attention``  -- causal softmax attention in binary64 over the dequantized
                     cache, for a mixed batch of chunk rows and decode rows.
+* ``scheduler``  -- the fair scheduler that decides each step's rows (bounded
+                    prefill chunk, decode first, decoder rotation, per-client
+                    quota, SRTF, starving-decode preemption, near-done gate)
+                    and builds the step's batch descriptor.
 
 Source pages (cited by title and section):
 
@@ -25,6 +29,8 @@ Source pages (cited by title and section):
   gives the KV modes table (q8: one f16 scale per 32 elements, 34 bytes; 4-bit
   values packed into 18 bytes), the codec bit-exactness statement, and the
   occupancy table ("佔用": bytes per position and per 262144-token session).
+  Section 1 also holds the scheduler rules: the table "排程器保證什麼" and the
+  fairness part "公平性：排隊不插隊".
 
 Parity status of each function is given in its docstring.  Every function here
 is pinned by a ``-m "not gpu"`` test against something other than itself
@@ -32,4 +38,4 @@ is pinned by a ``-m "not gpu"`` test against something other than itself
 case, or invariants), except where a docstring says "parity unpinned".
 """
 
-from . import codec, cache, attention  # noqa: F401
+from . import codec, cache, attention, scheduler  # noqa: F401

@@ -90,3 +90,104 @@ def test_attention_mutants_are_caught(monkeypatch, mutant):
         ta.test_brute_force_tiny("q8", "q4")
     with pytest.raises(AssertionError):
         ta.test_codec_free_case_matches_torch_sdpa()
+
+
+# --- scheduler oracle -------------------------------------------------------
+
+import numpy as np  # noqa: E402
+
+import test_oracle_scheduler as ts  # noqa: E402
+from oracle import scheduler as sched  # noqa: E402
+
+
+class _NoMarkAllDue(sched.Scheduler):
+    def step(self):
+        st = super().step()
+        if st is not None and st["kind"] == "merged":
+            for r in self.decode_queue:
+                r.due = False
+        return st
+
+
+class _FifoPrefill(sched.Scheduler):
+    def pick_chunk(self):
+        prefills = sorted((r for r in self.resident if r.state == "prefill"), key=lambda r: r.rid)
+        return prefills[0] if prefills else None
+
+
+class _NoGate(sched.Scheduler):
+    def pick_chunk(self):
+        prefills = sorted((r for r in self.resident if r.state == "prefill"), key=lambda r: r.rid)
+        near = [r for r in prefills if r.prompt - r.prefilled <= self.chunk]
+        far = [r for r in prefills if r.prompt - r.prefilled > self.chunk]
+        return (near + far)[0] if prefills else None
+
+
+class _NoRotation(sched.Scheduler):
+    def step(self):
+        st = super().step()
+        self.decode_queue.sort(key=lambda r: r.rid)
+        return st
+
+
+class _ChunkFirst(sched.Scheduler):
+    def step(self):
+        st = super().step()
+        if st is not None and st["kind"] == "merged" and len(st["ids"]) > 1:
+            chunk_row = [i for i, rid in enumerate(st["ids"]) if st["q_len"][i] > 1 or self.requests[rid].generated <= 1]
+            if chunk_row and chunk_row[-1] == len(st["ids"]) - 1:
+                for k in st:
+                    if k != "kind":
+                        st[k] = st[k][-1:] + st[k][:-1]
+        return st
+
+
+class _GlobalFifoAdmission(sched.Scheduler):
+    def admit(self):
+        while len(self.resident) < self.sessions and self.rotation:
+            waiting = sorted((q[0] for q in self.pending.values() if q), key=lambda r: r.rid)
+            r = waiting[0]
+            need = self.pages_needed(r.prompt, r.limit)
+            if need > len(self.free_pages):
+                break
+            self.pending[r.client].popleft()
+            self.free_pages.sort()
+            r.pages, self.free_pages = self.free_pages[:need], self.free_pages[need:]
+            r.state = "prefill"
+            self.resident.append(r)
+            self.rotation = [c for c in self.rotation if self.pending[c]]
+
+
+class _DecodePrefixOffByOne(sched.Scheduler):
+    def step(self):
+        st = super().step()
+        if st is not None:
+            st["prefix_len"] = [p + 1 if q == 1 and self.requests[rid].prefilled == self.requests[rid].prompt
+                                and p >= self.requests[rid].prompt - 1 else p
+                                for rid, p, q in zip(st["ids"], st["prefix_len"], st["q_len"])]
+        return st
+
+
+def _scheduler_pins(make):
+    for trace in ts.golden_traces():
+        got, pages = ts.run_golden(trace, make)
+        assert got == trace["steps"] and pages == trace["pages"]
+    for seed in range(40):
+        rng = np.random.default_rng(1000 + seed)
+        cfg = ts.random_config(rng)
+        arrivals = ts.random_arrivals(rng, int(rng.integers(20, 120)), int(rng.integers(1, 5)))
+        obs = ts.Observer(cfg)
+        ts.drive(make(**cfg), cfg, arrivals, obs)
+        obs.check_all_finished()
+        obs.check_admission_rotation()
+
+
+@pytest.mark.parametrize("mutant", [_NoMarkAllDue, _FifoPrefill, _NoGate, _NoRotation, _ChunkFirst,
+                                    _GlobalFifoAdmission, _DecodePrefixOffByOne], ids=lambda m: m.__name__)
+def test_scheduler_mutants_are_caught(mutant):
+    with pytest.raises(AssertionError):
+        _scheduler_pins(mutant)
+
+
+def test_scheduler_pins_pass_unmutated():
+    _scheduler_pins(sched.Scheduler)
