@@ -77,7 +77,8 @@ enum {
   MAB_ERR_UNSUPPORTED = 3, /* well-formed but outside the supported shapes     */
   MAB_ERR_WORKSPACE = 4,   /* workspace smaller than attention_workspace_bytes */
   MAB_ERR_ALIGN = 5,       /* a device buffer is not 16-byte aligned           */
-  MAB_ERR_HIP = 6          /* the HIP runtime refused a kernel launch          */
+  MAB_ERR_HIP = 6,         /* the HIP runtime refused a kernel launch          */
+  MAB_ERR_QUOTA = 7        /* mab_sched_submit: the client's pending cap is full */
 };
 
 /* KV block formats (MBufo page, section 2 modes table and occupancy table). */
@@ -196,6 +197,91 @@ const char* mab_status_string(int32_t status);
  * for all work on the current device first (every stream).  A debugging aid:
  * the pages define no error reporting of their own. */
 int32_t mab_debug_status(int32_t reset);
+
+/* ------------------------------------------------------------------------
+ * Step scheduler and batch builder (host only; no device memory).
+ *
+ * Decides each engine tick's rows and writes the tick's batch descriptor,
+ * following the scheduler rules of the MBufo page, section 1: the table of
+ * scheduler guarantees and the fairness part (SRTF, starving-decode
+ * preemption, near-done gate).
+ *
+ *  - Admission: pending requests take free session slots, clients taking
+ *    turns (FIFO within a client).  A request reserves its KV pages,
+ *    ceil((prompt_len + token_limit - 1) / page_size), at admission: the
+ *    lowest-numbered free pages.  Admission stops at the first request that
+ *    does not fit.
+ *  - Decode first: while some decoder is due, a tick is a decode step over
+ *    the due decoders in queue order.  Otherwise it is a merged step: one
+ *    prefill chunk slice of at most prefill_chunk tokens plus the decoders
+ *    at the head of the queue.  Either way a tick serves at most
+ *    max_decode_rows decoders.
+ *  - Served decoders move to the back of the queue (PopDecoder rotation).
+ *    After a merged step every resident decoder is due
+ *    (MarkAllDecodersDue).
+ *  - The chunk goes to the earliest request with at most one chunk left,
+ *    else to the earliest other prefill (SRTF).  While a request waits for a
+ *    slot and some decoder is within near_done_gate tokens of its limit,
+ *    prefills with more than one chunk left get no chunk.
+ *
+ * Positions: a chunk row covers prompt positions [prefix, prefix + q_len).
+ * A decoder that has produced g tokens feeds token g: one row with
+ * prefix_len = prompt_len + g - 1.  The last chunk of a prompt yields the
+ * request's first token.  A request that has produced token_limit tokens is
+ * finished, and its slot and pages are released at the end of that tick.
+ * ---------------------------------------------------------------------- */
+
+typedef struct mab_sched_config {
+  int32_t sessions;               /* resident requests at most (session slots), >= 1      */
+  int32_t prefill_chunk;          /* tokens of one prefill chunk slice at most, >= 1      */
+  int32_t max_pending_per_client; /* waiting requests per client at most, >= 1           */
+  int32_t near_done_gate;         /* tokens left that make a decoder "near done", >= 0   */
+  int32_t max_decode_rows;        /* decoders served per tick at most; 0: sessions       */
+  int32_t page_size;              /* tokens per KV page (the layout's page_size), >= 1    */
+  int32_t num_pages;              /* pages in the pool (the layout's num_pages), >= 1     */
+  int32_t max_pages_per_seq;      /* block-table row width, >= 1                          */
+} mab_sched_config;
+
+typedef struct mab_sched mab_sched; /* opaque; owned by the caller via create/destroy */
+
+typedef struct mab_step_info {
+  int32_t kind;     /* 0: nothing to run, 1: decode step, 2: merged step      */
+  int32_t num_seqs; /* sequences written to the step arrays                   */
+  int32_t num_rows; /* query rows = q_start[num_seqs]                         */
+  int32_t pending;  /* requests still waiting for a slot after this tick      */
+} mab_step_info;
+
+/* Creates a scheduler with every page free.  *out receives it (NULL on
+ * error).  Returns MAB_ERR_NULL or MAB_ERR_SHAPE (a field out of range). */
+int32_t mab_sched_create(const mab_sched_config* cfg, mab_sched** out);
+
+/* Frees a scheduler (NULL is allowed). */
+void mab_sched_destroy(mab_sched* s);
+
+/* Queues a request: client id >= 0, prompt_len >= 1 tokens, token_limit >= 1
+ * tokens to produce.  *request_id receives its id (0, 1, 2, ... in submit
+ * order) or -1.  MAB_ERR_SHAPE: a field out of range, or the request could
+ * never fit (more pages than max_pages_per_seq or num_pages).
+ * MAB_ERR_QUOTA: the client already has max_pending_per_client requests
+ * waiting. */
+int32_t mab_sched_submit(mab_sched* s, int32_t client, int32_t prompt_len, int32_t token_limit,
+                         int64_t* request_id);
+
+/* Runs one tick: admission, then the step's choice, then the state update
+ * (the step is taken as run).  Host arrays of `capacity` sequences, capacity
+ * >= max_decode_rows + 1 (MAB_ERR_SHAPE otherwise):
+ *   request_id[capacity], prefix_len[capacity], emit[capacity],
+ *   finished[capacity], q_start[capacity + 1],
+ *   block_table[capacity * max_pages_per_seq] (row-major, padded with -1).
+ * Sequences are the decoders in the order served (q_len 1), then the chunk
+ * slice if any.  emit[i] = 1 when row i's step yields a token of its request,
+ * finished[i] = 1 when that request is done.  q_start, prefix_len and
+ * block_table are the mab_batch fields of the step (copy them to the device
+ * for kv_append_quant and mixed_attention_fwd).  kind 0 writes only
+ * q_start[0] = 0. */
+int32_t mab_sched_step(mab_sched* s, mab_step_info* info, int64_t* request_id, int32_t* q_start,
+                       int32_t* prefix_len, int32_t* block_table, int32_t* emit, int32_t* finished,
+                       int32_t capacity);
 
 #ifdef __cplusplus
 }

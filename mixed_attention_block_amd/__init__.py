@@ -45,6 +45,18 @@ class Batch(ctypes.Structure):
                 ("prefix_len_host", ctypes.c_void_p)]
 
 
+class SchedConfig(ctypes.Structure):
+    _fields_ = [("sessions", ctypes.c_int32), ("prefill_chunk", ctypes.c_int32),
+                ("max_pending_per_client", ctypes.c_int32), ("near_done_gate", ctypes.c_int32),
+                ("max_decode_rows", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32)]
+
+
+class StepInfo(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("pending", ctypes.c_int32)]
+
+
 _lib_handle = None
 
 
@@ -67,6 +79,13 @@ def _lib():
         lib.mixed_attention_fwd.restype = i32
         lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
         lib.mab_debug_status.argtypes, lib.mab_debug_status.restype = [i32], i32
+        lib.mab_sched_create.argtypes = [ctypes.POINTER(SchedConfig), ctypes.POINTER(P)]
+        lib.mab_sched_create.restype = i32
+        lib.mab_sched_destroy.argtypes, lib.mab_sched_destroy.restype = [P], None
+        lib.mab_sched_submit.argtypes = [P, i32, i32, i32, ctypes.POINTER(i64)]
+        lib.mab_sched_submit.restype = i32
+        lib.mab_sched_step.argtypes = [P, ctypes.POINTER(StepInfo), P, P, P, P, P, P, i32]
+        lib.mab_sched_step.restype = i32
         _lib_handle = lib
     return _lib_handle
 
@@ -172,3 +191,94 @@ def mab_debug_status(reset=True):
     if st < 0:
         raise MabError(-st, "mab_debug_status")
     return st
+
+
+MAB_ERR_QUOTA = 7
+STEP_KINDS = {0: None, 1: "decode", 2: "merged"}
+
+
+class Step:
+    """One tick of ``Scheduler.step``: host int32 arrays of the step's batch
+    (``q_start``, ``prefix_len``, ``block_table``) plus ``request_id``, ``emit``
+    and ``finished`` per sequence."""
+
+    def __init__(self, kind, request_id, q_start, prefix_len, block_table, emit, finished, pending):
+        self.kind = kind
+        self.request_id = request_id
+        self.q_start = q_start
+        self.prefix_len = prefix_len
+        self.block_table = block_table
+        self.emit = emit
+        self.finished = finished
+        self.pending = pending
+
+    @property
+    def num_seqs(self):
+        return len(self.prefix_len)
+
+    @property
+    def q_len(self):
+        return np.diff(self.q_start)
+
+    def batch(self, device="cuda"):
+        """The step's ``BatchDesc`` with device copies of the descriptor."""
+        import torch
+        dev = [torch.from_numpy(np.ascontiguousarray(a)).to(device)
+               for a in (self.q_start, self.prefix_len, self.block_table)]
+        return BatchDesc(dev[0], dev[1], dev[2], self.q_start, self.prefix_len)
+
+
+class Scheduler:
+    """The library's step scheduler (``mab_sched_*``): submit requests, then
+    call ``step()`` once per engine tick."""
+
+    def __init__(self, sessions, prefill_chunk, max_pending_per_client, near_done_gate, page_size,
+                 num_pages, max_pages_per_seq, max_decode_rows=0):
+        self.config = SchedConfig(sessions, prefill_chunk, max_pending_per_client, near_done_gate,
+                                  max_decode_rows, page_size, num_pages, max_pages_per_seq)
+        lib = _lib()
+        handle = ctypes.c_void_p()
+        st = lib.mab_sched_create(ctypes.byref(self.config), ctypes.byref(handle))
+        if st:
+            raise MabError(st, "mab_sched_create")
+        self._h = handle
+        self._lib = lib
+        self.capacity = (max_decode_rows or sessions) + 1
+        cap, width = self.capacity, max_pages_per_seq
+        self._ids = np.zeros(cap, np.int64)
+        self._qs = np.zeros(cap + 1, np.int32)
+        self._pl = np.zeros(cap, np.int32)
+        self._bt = np.zeros(cap * width, np.int32)
+        self._emit = np.zeros(cap, np.int32)
+        self._fin = np.zeros(cap, np.int32)
+        self._info = StepInfo()
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.mab_sched_destroy(h)
+            self._h = None
+
+    def submit(self, client, prompt_len, token_limit):
+        """Returns (status, request id): status 0, or MAB_ERR_QUOTA (7) / 2
+        with id -1.  Other failures raise."""
+        rid = ctypes.c_int64(-1)
+        st = self._lib.mab_sched_submit(self._h, client, prompt_len, token_limit, ctypes.byref(rid))
+        if st not in (0, 2, MAB_ERR_QUOTA):
+            raise MabError(st, "mab_sched_submit")
+        return st, rid.value
+
+    def step(self):
+        """One tick; None when there is nothing to run, else a ``Step``."""
+        st = self._lib.mab_sched_step(self._h, ctypes.byref(self._info), self._ids.ctypes.data,
+                                      self._qs.ctypes.data, self._pl.ctypes.data, self._bt.ctypes.data,
+                                      self._emit.ctypes.data, self._fin.ctypes.data, self.capacity)
+        if st:
+            raise MabError(st, "mab_sched_step")
+        info = self._info
+        if info.kind == 0:
+            return None
+        n, width = info.num_seqs, self.config.max_pages_per_seq
+        return Step(STEP_KINDS[info.kind], self._ids[:n].copy(), self._qs[:n + 1].copy(),
+                    self._pl[:n].copy(), self._bt[:n * width].reshape(n, width).copy(),
+                    self._emit[:n].copy(), self._fin[:n].copy(), info.pending)

@@ -1942,6 +1942,7 @@ const char* mab_status_string(int32_t status) {
     case MAB_ERR_WORKSPACE: return "workspace smaller than attention_workspace_bytes()";
     case MAB_ERR_ALIGN: return "a device buffer is not 16-byte aligned";
     case MAB_ERR_HIP: return "the HIP runtime refused a kernel launch";
+    case MAB_ERR_QUOTA: return "client_quota: the client's pending requests are at their cap";
     default: return "unknown status";
   }
 }
