@@ -257,3 +257,49 @@ def subset(case, seqs):
     other.k_prefix = [case.k_prefix[s] for s in seqs]
     other.v_prefix = [case.v_prefix[s] for s in seqs]
     return other, rows
+
+
+# --- serving-loop inputs ------------------------------------------------------
+
+def token_values(seed, request_ids, positions, hq, hkv, d):
+    """Query, key and value of the token at ``positions[i]`` of request
+    ``request_ids[i]``: fp16 numpy arrays [n, Hq, D], [n, Hkv, D], [n, Hkv, D].
+    Each token's values depend only on (seed, request, position), so a serving
+    loop and a checker that see the same tokens in different batches draw the
+    same numbers."""
+    n = len(positions)
+    q = np.empty((n, hq, d), np.float16)
+    k = np.empty((n, hkv, d), np.float16)
+    v = np.empty((n, hkv, d), np.float16)
+    for i, (rid, pos) in enumerate(zip(request_ids, positions)):
+        rng = np.random.default_rng([seed, int(rid), int(pos)])
+        x = rng.standard_normal((hq + 2 * hkv, d), dtype=np.float32).astype(np.float16)
+        q[i], k[i], v[i] = x[:hq], x[hq:hq + hkv], x[hq + hkv:]
+    return q, k, v
+
+
+SCENARIOS = ("chat16_long250k", "five_into_four")
+
+
+def serving_arrivals(name, seed):
+    """Arrivals (time in s, client, prompt tokens, token limit), sorted by time.
+
+    * ``chat16_long250k`` -- 16 clients chatting (prompts uniform in
+      [200, 2000] tokens, 64-256 output tokens, arrivals uniform over the
+      first 50 ms) while a 250000-token prompt (16 output tokens) arrives at
+      10 ms from client 16: the long-prompt-in-the-middle case.
+    * ``five_into_four`` -- four slots, five requests: a 120000-token prompt
+      and three chats at t = 0 (500-token prompts, 400 / 800 / 1600 output
+      tokens), then a short request (300 tokens, 64 out) at 20 ms that must
+      wait for a slot."""
+    rng = np.random.default_rng(seed)
+    if name == "chat16_long250k":
+        out = [(float(rng.uniform(0, 0.05)), c, int(rng.integers(200, 2001)), int(rng.integers(64, 257)))
+               for c in range(16)]
+        out.append((0.01, 16, 250000, 16))
+    elif name == "five_into_four":
+        out = [(0.0, 0, 120000, 32), (0.0, 1, 500, 400), (0.0, 2, 500, 800), (0.0, 3, 500, 1600),
+               (0.02, 4, 300, 64)]
+    else:
+        raise KeyError(name)
+    return sorted(out, key=lambda a: (a[0], a[1]))
