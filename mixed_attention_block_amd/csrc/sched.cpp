@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <climits>
 #include <deque>
 #include <functional>
 #include <new>
@@ -150,6 +151,7 @@ int32_t mab_sched_submit(mab_sched* s, int32_t client, int32_t prompt_len, int32
   if (!s || !request_id) return MAB_ERR_NULL;
   *request_id = -1;
   if (client < 0 || prompt_len < 1 || token_limit < 1) return MAB_ERR_SHAPE;
+  if ((int64_t)prompt_len + token_limit - 1 > INT32_MAX) return MAB_ERR_SHAPE;  // positions are int32
   const int64_t need = pages_for(prompt_len, token_limit, s->cfg.page_size);
   if (need > s->cfg.max_pages_per_seq || need > s->cfg.num_pages) return MAB_ERR_SHAPE;
   std::deque<int64_t>& w = s->waiting[client];

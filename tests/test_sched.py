@@ -113,6 +113,8 @@ def test_errors():
     assert s.submit(-1, 4, 4) == (2, -1)
     assert s.submit(0, 0, 4) == (2, -1)
     assert s.submit(0, 60, 6) == (2, -1)          # 65 positions: 5 pages > 4
+    big = mab.Scheduler(2, 8, 2, 4, page_size=1 << 20, num_pages=1 << 12, max_pages_per_seq=1 << 12)
+    assert big.submit(0, 2**31 - 1, 2) == (2, -1)  # positions past int32
     assert s.submit(0, 60, 5) == (0, 0)
     assert s.submit(0, 1, 1) == (0, 1)
     assert s.submit(0, 1, 1) == (mab.MAB_ERR_QUOTA, -1)
