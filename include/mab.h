@@ -260,8 +260,9 @@ void mab_sched_destroy(mab_sched* s);
 
 /* Queues a request: client id >= 0, prompt_len >= 1 tokens, token_limit >= 1
  * tokens to produce.  *request_id receives its id (0, 1, 2, ... in submit
- * order) or -1.  MAB_ERR_SHAPE: a field out of range, or the request could
- * never fit (more pages than max_pages_per_seq or num_pages).
+ * order) or -1.  MAB_ERR_SHAPE: a field out of range, positions past int32
+ * (prompt_len + token_limit - 1 > INT32_MAX), or a request that could never
+ * fit (more pages than max_pages_per_seq or num_pages).
  * MAB_ERR_QUOTA: the client already has max_pending_per_client requests
  * waiting. */
 int32_t mab_sched_submit(mab_sched* s, int32_t client, int32_t prompt_len, int32_t token_limit,
