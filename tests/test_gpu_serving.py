@@ -33,6 +33,10 @@ CASES = [
      dict(sessions=4, prefill_chunk=40, max_pending_per_client=4, near_done_gate=6), 71),
     ("k4v4_g6_p32", dict(hq=12, hkv=2, d=128, ps=32, kf="q4", vf="q4"),
      dict(sessions=3, prefill_chunk=24, max_pending_per_client=2, near_done_gate=3, max_decode_rows=2), 72),
+    ("f16_g8_p64", dict(hq=8, hkv=1, d=128, ps=64, kf="f16", vf="f16"),
+     dict(sessions=5, prefill_chunk=33, max_pending_per_client=3, near_done_gate=5), 73),
+    ("k8v4_g2_p48", dict(hq=4, hkv=2, d=64, ps=48, kf="q8", vf="q4"),
+     dict(sessions=4, prefill_chunk=17, max_pending_per_client=4, near_done_gate=2, max_decode_rows=3), 74),
 ]
 
 
