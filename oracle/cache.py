@@ -74,15 +74,6 @@ def gather_tokens(pool, layout, fmt, table_row, length):
     return out
 
 
-def gather_blocks(pool, layout, table_row, length):
-    """Raw block bytes of positions [0, length): uint8 [length, Hkv, D/32, B]."""
-    ps = layout["page_size"]
-    pos = np.arange(length, dtype=np.int64)
-    pages = np.asarray(table_row, dtype=np.int64)[pos // ps]
-    slots = pos % ps
-    return pool[pages, :, slots]
-
-
 def append(k_pool, v_pool, layout, q_start, prefix_len, block_table, k_new, v_new):
     """The append step: row i of sequence s is written at position
     ``prefix_len[s] + i`` (its own position), keys to ``k_pool`` and values to

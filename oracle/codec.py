@@ -60,13 +60,6 @@ def qmax(fmt):
     return _FORMATS[fmt][1]
 
 
-def bytes_per_value(fmt):
-    """Storage bytes per cached value: 34/32 (q8), 18/32 (q4), 2 (f16)."""
-    if fmt == "f16":
-        return 2.0
-    return block_bytes(fmt) / VALUES_PER_BLOCK
-
-
 def bytes_per_position(num_kv_heads, head_dim, k_fmt, v_fmt):
     """KV bytes per token position per layer (K plus V).
 
