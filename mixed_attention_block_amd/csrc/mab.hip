@@ -84,6 +84,12 @@ constexpr int kMinWaveStages = 4;   // a decode work-group streams at least this
 constexpr int kDecodeDepth = 1;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // a row keeps a stale max until it is 2^8 behind
+// Decode weights P (up to 2^kRescaleSlack under the stale max) are multiplied
+// by the V block scale in fp16.  A stage holding a V scale at or above this
+// bound (fp16 bits; 128.0) takes the exact running max instead (P <= 1), so
+// P * scale stays below 2^15 in every stage whatever the scale (at most 9360,
+// the 4-bit scale of a block at the fp16 maximum).
+constexpr uint16_t kBigVScaleBits = 0x5800u;
 constexpr float kDecodeMaxFloor = -1e30f;  // initial running max of a decode slot (log2 units)
 
 template <int F> struct Fmt;
@@ -518,9 +524,12 @@ struct DecWave {
 // K scales as fp32 times c = sm_scale*log2(e), V scales as fp16, both [block][key].
 // Keys at or past kend get scale 0, so their (possibly NaN) bytes never reach
 // a sum: their logits become exactly 0 before masking and their P*scale 0.
+// Returns (wave-uniform) whether some V scale of the stage is at or above
+// kBigVScaleBits.
 template <int NB, int KF, int VF>
-__device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
+__device__ inline bool dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
   using L = DecLayout<NB, KF, VF>;
+  bool big = false;
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     const int idx = lane + 64 * q;            // NB*64 = 2*32*NB entries: K first, then V
@@ -539,20 +548,24 @@ __device__ inline void dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
       if constexpr (VF != MAB_KV_F16)
         bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
       reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = ok ? bits : (uint16_t)0;
+      big |= ok && bits >= kBigVScaleBits;  // scales are non-negative: bit order is value order
     }
   }
+  return __any(big);
 }
 
 // One 32-key stage of a decode wave: S^T = K Q^T on integer codes per block,
 // fp32 block scales, online softmax with a stale max (rescaled only when the
-// running max grows by more than 2^kRescaleSlack), then O^T += V^T (P * V
-// scale) with P rounded to fp16 once and multiplied by the fp16 V scale of
-// each block.  The V codes enter with the bias of their conversion; the sum
-// of each block's weights (an MFMA against ones) removes it at the end.
-// `tail`: the stage holds keys at or past kend, or past the limit of some
-// slot (masked per slot).
+// running max grows by more than 2^kRescaleSlack; by any amount in a stage
+// with a large V scale, `big_v`), then O^T += V^T (P * V scale) with P
+// rounded to fp16 once and multiplied by the fp16 V scale of each block.  The
+// normaliser sums the same fp16 P.  The V codes enter with the bias of their
+// conversion; the sum of each block's weights (an MFMA against ones) removes
+// it at the end.  `tail`: the stage holds keys at or past kend, or past the
+// limit of some slot (masked per slot).
 template <int NB, int KF, int VF>
-__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, int lane) {
+__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, bool big_v,
+                                   int lane) {
   // keys visible to this lane's slot in the stage: below kend and at most gr.limit
   using L = DecLayout<NB, KF, VF>;
   const int j = lane >> 4, n = lane & 15;
@@ -583,7 +596,7 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   mx = max_xor32(max_xor16(mx));
-  const bool grow = mx > gr.m + kRescaleSlack;  // also true for the first keys (m = -inf)
+  const bool grow = mx > gr.m + (big_v ? 0.f : kRescaleSlack);  // also true for the first keys (m = -inf)
   if (__any(grow)) {
     const float m_new = grow ? mx : gr.m;
     const float alpha = grow ? __builtin_amdgcn_exp2f(gr.m - m_new) : 1.f;  // 0 when m was -inf
@@ -595,18 +608,21 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     gr.m = m_new;
   }
   float p[8];
-  float psum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][i] - gr.m);  // <= 2^kRescaleSlack; masked keys 0
-      psum += p[4 * kt + i];
-    }
-  gr.l += psum;
+    for (int i = 0; i < 4; ++i)
+      p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][i] - gr.m);  // <= 2^kRescaleSlack (1 if big_v); masked 0
   // P as fp16 in the key order of the PV operand: 4j+[0,4) then 16+4j+[0,4)
   const half8_t ph = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
                              (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
+  // the normaliser sums the fp16 weights that the PV products use
+  const half2_t one2 = half2_t{(half_t)1.f, (half_t)1.f};
+  float psum = __builtin_amdgcn_fdot2(half2_t{ph[0], ph[1]}, one2, 0.f, false);
+  psum = __builtin_amdgcn_fdot2(half2_t{ph[2], ph[3]}, one2, psum, false);
+  psum = __builtin_amdgcn_fdot2(half2_t{ph[4], ph[5]}, one2, psum, false);
+  psum = __builtin_amdgcn_fdot2(half2_t{ph[6], ph[7]}, one2, psum, false);
+  gr.l += psum;
   const half_t* sv = reinterpret_cast<const half_t*>(w + L::kSVOff);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -1078,10 +1094,10 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
     const int kbase = kb + st * kStepKeys;
     dw.store(wbuf, lane);
     asm volatile("" ::: "memory");
-    dec_scales<NB, KF, VF>(wbuf, lane, a.c, ke - kbase);
+    const bool big_v = dec_scales<NB, KF, VF>(wbuf, lane, a.c, ke - kbase);
     if (st + DEPTH < nst) issue(dw, st + DEPTH);
     asm volatile("" ::: "memory");
-    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > kvis, lane);
+    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > kvis, big_v, lane);
     asm volatile("" ::: "memory");
   };
 #pragma unroll
@@ -1844,9 +1860,14 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch, con
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
 
-int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
-                            const void* k_pool, const void* v_pool, float sm_scale, float* out,
-                            void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The body of mixed_attention_fwd.
+int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, const void* q, const void* k_pool,
+                       const void* v_pool, float sm_scale, float* out, void* workspace, int64_t workspace_bytes,
+                       void* stream, int32_t too_small) {
   int st = check_layout(layout);
   if (st) return st;
   HostPlan hp;
@@ -1858,7 +1879,7 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
     return MAB_ERR_ALIGN;
   const WsLayout wl = plan_ws(layout, hp);
-  if (workspace_bytes < wl.total) return MAB_ERR_WORKSPACE;
+  if (workspace_bytes < wl.total) return too_small;
 
   char* ws = (char*)workspace;
   AttnArgs a;
@@ -1920,6 +1941,17 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
     }
   }
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
+                            const void* k_pool, const void* v_pool, float sm_scale, float* out,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+  return attention_call(layout, batch, q, k_pool, v_pool, sm_scale, out, workspace, workspace_bytes, stream,
+                        MAB_ERR_WORKSPACE);
 }
 
 int32_t mab_debug_status(int32_t reset) {
