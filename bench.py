@@ -52,6 +52,91 @@ SEEDS = {"decode16": 2, "decode16_f16": 2, "verify16": 6, "mixed16_chunk2k": 3, 
          "step_k4v4": 5}
 
 
+POISON = 0x7E  # bytes of pool space no append has written (fp16 NaN scales)
+
+
+class DeviceCase:
+    """One layer's device state: pools written by kv_append_quant (the cached
+    prefix first, then the step's rows at their own positions), the batch
+    descriptor, the step's inputs, an output buffer and the workspace."""
+
+    def __init__(self, case):
+        import torch
+        import mixed_attention_block_amd as mab
+
+        lay = case.layout
+        self.case = case
+        self.layout = mab.make_layout(lay["num_q_heads"], lay["num_kv_heads"], lay["head_dim"],
+                                      lay["page_size"], lay["num_pages"], lay["k_format"], lay["v_format"])
+        self.k_pool = torch.full((mab.kv_pool_bytes(self.layout, lay["k_format"]),), POISON,
+                                 dtype=torch.uint8, device="cuda")
+        self.v_pool = torch.full((mab.kv_pool_bytes(self.layout, lay["v_format"]),), POISON,
+                                 dtype=torch.uint8, device="cuda")
+        self.batch = self._batch(case.q_start, case.prefix_len, case.block_table)
+        # the cached prefix: one append over every sequence that has one
+        keep = [s for s in range(case.num_seqs) if case.prefix_len[s] > 0]
+        if keep:
+            rows = case.prefix_len[keep].astype(np.int64)
+            fill = self._batch(np.concatenate([[0], np.cumsum(rows)]), np.zeros(len(keep)),
+                               case.block_table[keep])
+            k = torch.cat([case.k_prefix[s] for s in keep]).cuda().contiguous()
+            v = torch.cat([case.v_prefix[s] for s in keep]).cuda().contiguous()
+            mab.kv_append_quant(self.layout, fill, k, v, self.k_pool, self.v_pool)
+            del k, v
+        self.q = case.q.cuda().contiguous()
+        self.k_new = case.k_new.cuda().contiguous()
+        self.v_new = case.v_new.cuda().contiguous()
+        mab.kv_append_quant(self.layout, self.batch, self.k_new, self.v_new, self.k_pool, self.v_pool)
+        self.out = torch.empty((case.num_rows, lay["num_q_heads"], lay["head_dim"]), dtype=torch.float32,
+                               device="cuda")
+        n = mab.attention_workspace_bytes(self.layout, self.batch)
+        self.ws = torch.empty((max(n, 256),), dtype=torch.uint8, device="cuda")
+
+    @staticmethod
+    def _batch(q_start, prefix_len, block_table):
+        import torch
+        import mixed_attention_block_amd as mab
+
+        qs = np.ascontiguousarray(q_start, dtype=np.int32)
+        pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        return mab.BatchDesc(torch.from_numpy(qs).cuda(), torch.from_numpy(pl).cuda(),
+                             torch.from_numpy(bt).cuda(), qs, pl)
+
+
+def realism_probes(stream):
+    """What this device reaches on plain work: a 4 GiB stream read (GB/s) and
+    dense 16x16x32 fp16 matrix-core products (TFLOP/s), each the best of
+    five runs timed with events on the benchmark's stream."""
+    import torch
+    import mixed_attention_block_amd as mab
+
+    buf = torch.empty((4 << 30,), dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_rd = best_mf = 0.0
+    mab.mab_probe_stream_read(buf, sink, stream)  # warm-up
+    mab.mab_probe_mfma_f16(2000, sink, stream)
+    for _ in range(5):
+        e0.record(stream)
+        n = mab.mab_probe_stream_read(buf, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best_rd = max(best_rd, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        e0.record(stream)
+        f = mab.mab_probe_mfma_f16(20000, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best_mf = max(best_mf, f / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    del buf
+    return {"stream_read_gbs": round(best_rd, 1), "stream_read_bytes": 4 << 30,
+            "mfma_f16_tflops": round(best_mf, 1),
+            "note": "mab_probe_stream_read (16-byte non-temporal loads over 4 GiB) and "
+                    "mab_probe_mfma_f16 (independent 16x16x32 fp16 products, 2 waves per SIMD), "
+                    "best of 5"}
+
+
 def kv_bytes_per_position(layout):
     from mixed_attention_block_amd import kv_block_bytes
     nb = layout["head_dim"] // 32
@@ -78,7 +163,6 @@ def cpu_baseline(case, budget_s=12.0):
     import torch
     from threadpoolctl import threadpool_info
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import attention as oattn
     from oracle import cache as ocache
 
@@ -232,7 +316,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="step_k4v4", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -246,8 +330,6 @@ def main():
 
     import mixed_attention_block_amd as mab
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_harness import GpuState
 
     torch.cuda.set_device(0)
     name = args.workload
@@ -263,18 +345,11 @@ def main():
     for layer in range(layers):
         case = synth.make_case(name, seed, device="cuda",
                                value_seed=seed * 100 + layer if layers > 1 else None)
-        st = GpuState(case)
-        st.append_step()
+        st = DeviceCase(case)
         bpp = kv_bytes_per_position(case.layout)
         kv_bytes += sum(case.context(s) for s in range(case.num_seqs)) * bpp
         rows = case.num_rows  # the layers share one batch
         flops += chunk_flops(case)
-        st.q = case.q.contiguous()
-        st.k_new = case.k_new.contiguous()
-        st.v_new = case.v_new.contiguous()
-        st.ws = st.workspace()
-        st.out = torch.empty((case.num_rows, case.layout["num_q_heads"], case.layout["head_dim"]),
-                             dtype=torch.float32, device="cuda")
         if first_case is None:
             first_case = case
         else:  # keep only what the timed loop needs
@@ -416,6 +491,7 @@ def main():
         }
         if "traffic_detail" in hbm:
             result["roofline"]["traffic_detail"] = hbm["traffic_detail"]
+    result["roofline"]["realism"] = realism_probes(stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(first_case)
     print(json.dumps(result), flush=True)

@@ -199,6 +199,27 @@ const char* mab_status_string(int32_t status);
 int32_t mab_debug_status(int32_t reset);
 
 /* ------------------------------------------------------------------------
+ * Measurement probes.  No passage of the pages defines them: they measure
+ * what this device reaches on plain work, the realism lines beside the
+ * roofline fractions of the attention calls.  Both enqueue one kernel on
+ * `stream` and return at once.
+ * ---------------------------------------------------------------------- */
+
+/* Reads `bytes` (a multiple of 16, >= 16) of device memory at `buf` (16-byte
+ * aligned) once, with 16-byte non-temporal loads, eight 256-thread
+ * work-groups per compute unit, sixteen loads in flight per thread.  `sink`:
+ * 16 bytes of device memory (16-byte aligned), practically never written.  Time it
+ * with events on `stream`; bytes / time is the device's stream-read rate.
+ * Returns MAB_OK, MAB_ERR_NULL, MAB_ERR_SHAPE, MAB_ERR_ALIGN or MAB_ERR_HIP. */
+int32_t mab_probe_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
+
+/* Runs `iters` (>= 1) rounds of eight independent 16x16x32 fp16 matrix-core
+ * products per wave, two 4-wave work-groups per compute unit.  `sink`: 16
+ * bytes of device memory (16-byte aligned), practically never written.
+ * Returns the flops enqueued (2*16*16*32 per product), or a negative status. */
+int64_t mab_probe_mfma_f16(int32_t iters, void* sink, void* stream);
+
+/* ------------------------------------------------------------------------
  * Step scheduler and batch builder (host only; no device memory).
  *
  * Decides each engine tick's rows and writes the tick's batch descriptor,

@@ -79,6 +79,9 @@ def _lib():
         lib.mixed_attention_fwd.restype = i32
         lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
         lib.mab_debug_status.argtypes, lib.mab_debug_status.restype = [i32], i32
+        lib.mab_probe_stream_read.argtypes = [P, i64, P, P]
+        lib.mab_probe_stream_read.restype = i32
+        lib.mab_probe_mfma_f16.argtypes, lib.mab_probe_mfma_f16.restype = [i32, P, P], i64
         lib.mab_sched_create.argtypes = [ctypes.POINTER(SchedConfig), ctypes.POINTER(P)]
         lib.mab_sched_create.restype = i32
         lib.mab_sched_destroy.argtypes, lib.mab_sched_destroy.restype = [P], None
@@ -191,6 +194,23 @@ def mab_debug_status(reset=True):
     if st < 0:
         raise MabError(-st, "mab_debug_status")
     return st
+
+
+def mab_probe_stream_read(buf, sink, stream=None):
+    """Enqueue one stream read of the device tensor ``buf`` (its whole storage)."""
+    nbytes = buf.numel() * buf.element_size()
+    st = _lib().mab_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream_handle(stream))
+    if st:
+        raise MabError(st, "mab_probe_stream_read")
+    return nbytes
+
+
+def mab_probe_mfma_f16(iters, sink, stream=None):
+    """Enqueue the dense fp16 matrix-core probe; returns the flops enqueued."""
+    n = _lib().mab_probe_mfma_f16(int(iters), sink.data_ptr(), _stream_handle(stream))
+    if n < 0:
+        raise MabError(-n, "mab_probe_mfma_f16")
+    return n
 
 
 MAB_ERR_QUOTA = 7

@@ -11,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mab.hip")
 SCHED = os.path.join(HERE, "csrc", "sched.cpp")  # host code: the step scheduler
+PROBE = os.path.join(HERE, "csrc", "probe.hip")  # measurement probes (stream read, dense MFMA)
 OUT = os.path.join(HERE, "libmab.so")
 
 FLAGS = [
@@ -28,7 +29,7 @@ FLAGS = [
 def build(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc] + FLAGS + [SRC, SCHED, "-o", tmp]
+    cmd = [hipcc] + FLAGS + [SRC, PROBE, SCHED, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
