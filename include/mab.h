@@ -78,7 +78,9 @@ enum {
   MAB_ERR_WORKSPACE = 4,   /* workspace smaller than attention_workspace_bytes */
   MAB_ERR_ALIGN = 5,       /* a device buffer is not 16-byte aligned           */
   MAB_ERR_HIP = 6,         /* the HIP runtime refused a kernel launch          */
-  MAB_ERR_QUOTA = 7        /* mab_sched_submit: the client's pending cap is full */
+  MAB_ERR_QUOTA = 7,       /* mab_sched_submit: the client's pending cap is full */
+  MAB_ERR_SCRATCH = 8      /* mixed_attention_fwd_noalloc: the batch needs more
+                              than MAB_NOALLOC_SCRATCH_BYTES of workspace      */
 };
 
 /* KV block formats (MBufo page, section 2 modes table and occupancy table). */
@@ -177,6 +179,28 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
                             const void* q, const void* k_pool, const void* v_pool,
                             float sm_scale, float* out,
                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* mixed_attention_fwd_noalloc: mixed_attention_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operation, arguments, results and
+ * determinism as mixed_attention_fwd; the workspace is instead a fixed array
+ * of MAB_NOALLOC_SCRATCH_BYTES owned by the library, one per device, which
+ * each device that runs the call holds until the process ends.  The call
+ * allocates nothing (the array's device address is looked up once per
+ * device, on the first call with that device current).
+ *
+ * The caller still owns q, the pools and out.  A batch whose
+ * attention_workspace_bytes() exceeds MAB_NOALLOC_SCRATCH_BYTES returns
+ * MAB_ERR_SCRATCH before anything is enqueued.  The array needs no
+ * initialisation and keeps whatever the last call left in it.  Every call on
+ * one device shares that device's array: calls that may overlap on one
+ * device (several streams, several host threads) race and give undefined
+ * results; serialise them, or use mixed_attention_fwd with distinct
+ * workspaces. */
+#define MAB_NOALLOC_SCRATCH_BYTES (128LL << 20)
+int32_t mixed_attention_fwd_noalloc(const mab_kv_layout* layout, const mab_batch* batch,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    float sm_scale, float* out, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* mab_status_string(int32_t status);

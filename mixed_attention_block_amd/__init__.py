@@ -77,6 +77,8 @@ def _lib():
         lib.kv_append_quant.restype = i32
         lib.mixed_attention_fwd.argtypes = [lay, bat, P, P, P, f32, P, P, i64, P]
         lib.mixed_attention_fwd.restype = i32
+        lib.mixed_attention_fwd_noalloc.argtypes = [lay, bat, P, P, P, f32, P, P]
+        lib.mixed_attention_fwd_noalloc.restype = i32
         lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
         lib.mab_debug_status.argtypes, lib.mab_debug_status.restype = [i32], i32
         lib.mab_probe_stream_read.argtypes = [P, i64, P, P]
@@ -181,6 +183,23 @@ def mixed_attention_fwd(layout, batch, q, k_pool, v_pool, sm_scale, out, workspa
                                     workspace.numel(), _stream_handle(stream))
     if st:
         raise MabError(st, "mixed_attention_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MAB_NOALLOC_SCRATCH_BYTES
+
+
+def mixed_attention_fwd_noalloc(layout, batch, q, k_pool, v_pool, sm_scale, out, stream=None):
+    """mixed_attention_fwd with the library's fixed per-device scratch array
+    as workspace (no allocation; overlapping calls on one device race)."""
+    _check_tensor(q, "float16", "q")
+    _check_tensor(k_pool, "uint8", "k_pool")
+    _check_tensor(v_pool, "uint8", "v_pool")
+    _check_tensor(out, "float32", "out")
+    st = _lib().mixed_attention_fwd_noalloc(ctypes.byref(layout), ctypes.byref(batch.struct),
+                                            q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                            float(sm_scale), out.data_ptr(), _stream_handle(stream))
+    if st:
+        raise MabError(st, "mixed_attention_fwd_noalloc")
 
 
 def mab_status_string(status):

@@ -22,6 +22,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "mab.h"
@@ -1864,7 +1865,7 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch, con
 
 namespace {
 
-// The body of mixed_attention_fwd.
+// The common body of mixed_attention_fwd and mixed_attention_fwd_noalloc.
 int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, const void* q, const void* k_pool,
                        const void* v_pool, float sm_scale, float* out, void* workspace, int64_t workspace_bytes,
                        void* stream, int32_t too_small) {
@@ -1943,6 +1944,32 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   return hipGetLastError() == hipSuccess ? MAB_OK : MAB_ERR_HIP;
 }
 
+// The workspace of mixed_attention_fwd_noalloc: one array per device, held
+// from the module's load on that device until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, taken once per device.
+constexpr int64_t kScratchBytes = MAB_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).
+int32_t scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAB_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MAB_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MAB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1952,6 +1979,16 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
                             void* workspace, int64_t workspace_bytes, void* stream) {
   return attention_call(layout, batch, q, k_pool, v_pool, sm_scale, out, workspace, workspace_bytes, stream,
                         MAB_ERR_WORKSPACE);
+}
+
+int32_t mixed_attention_fwd_noalloc(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
+                                    const void* k_pool, const void* v_pool, float sm_scale, float* out,
+                                    void* stream) {
+  void* ws = nullptr;
+  const int32_t st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return attention_call(layout, batch, q, k_pool, v_pool, sm_scale, out, ws, kScratchBytes, stream,
+                        MAB_ERR_SCRATCH);
 }
 
 int32_t mab_debug_status(int32_t reset) {
@@ -1975,6 +2012,7 @@ const char* mab_status_string(int32_t status) {
     case MAB_ERR_ALIGN: return "a device buffer is not 16-byte aligned";
     case MAB_ERR_HIP: return "the HIP runtime refused a kernel launch";
     case MAB_ERR_QUOTA: return "client_quota: the client's pending requests are at their cap";
+    case MAB_ERR_SCRATCH: return "the batch needs more workspace than the fixed scratch array of the no-allocation call";
     default: return "unknown status";
   }
 }
