@@ -71,6 +71,9 @@ __device__ inline int checked_page(int page, int num_pages, int debug) {
   return page;
 }
 
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 constexpr int kDecodeWaves = 4;     // waves of a decode-kernel work-group (two work-groups per CU)
 constexpr int kMixedWaves = 8;      // waves of a mixed-kernel work-group (one per CU)
 constexpr int kStepKeys = 32;       // keys per stage / tile
@@ -679,7 +682,7 @@ struct ChunkTile {
   static constexpr int kStride = kD + 8;   // halves per key row: rows 16 bytes apart modulo 256
   half_t k[kStepKeys * kStride];           // K codes (exact integers)
   half_t v[kStepKeys * kStride];           // fp16(V code * scale)
-  half_t kd[NB * kStepKeys];               // K block scale (exact), [block][key]
+  float kd[NB * kStepKeys];                // K block scale times c = sm_scale*log2(e), [block][key]
 };
 
 // Value index (0..31 within a block) held at position p of a block's LDS row
@@ -739,7 +742,8 @@ __device__ inline uint32_t raw_scale(const ChunkRaw& r) { return SH ? r.w[0] >> 
 // the range (its bytes come from a valid key) gets scale 0: K logits and V
 // values of 0, never a stray NaN.
 template <int NB, int KF, int VF, int SH>
-__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid) {
+__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid,
+                                        float c) {
   using T = ChunkTile<NB>;
   const int F = is_v ? VF : KF;
   half_t d;
@@ -770,7 +774,7 @@ __device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, boo
   } else {
 #pragma unroll
     for (int g8 = 0; g8 < 4; ++g8) *reinterpret_cast<half8_t*>(row + 8 * g8) = out[g8];
-    t.kd[b * kStepKeys + key] = d;
+    t.kd[b * kStepKeys + key] = (float)d * c;
   }
 }
 
@@ -789,7 +793,7 @@ struct ChunkWave {
   half8_t q[2][NB];    // Q^T operand: row 16*rt + l%16, block b, slots 8*(l/16) + [0,8)
   float4_t o[2][2 * NB];  // O^T: tile rt, dim slots 16*dt + 4*(l/16) + [0,4)
   float4_t l[2];       // row sums of P, from an MFMA against ones (all four entries equal)
-  float m[2];          // running (stale) max of the raw logits
+  float m[2];          // running (stale) max of the logits, in exp2 units (-inf: no key yet)
   int limit[2];        // last visible key of the lane's row (-1 past the rows)
 };
 
@@ -843,17 +847,23 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
         pb[kt][b][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, cw.q[rt][b], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
   }
+  // s = c * (Q K^T) - m in exp2 units: each logit's chain of block-scale FMAs
+  // (scales already times c) starts from -m, the row's stale max (0 for a
+  // row with no key yet), so P = exp2(s) needs no further arithmetic
+  float base[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) base[rt] = cw.m[rt] == -INFINITY ? 0.f : -cw.m[rt];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    s[kt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-    s[kt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    s[kt][0] = float4_t{base[0], base[0], base[0], base[0]};
+    s[kt][1] = float4_t{base[1], base[1], base[1], base[1]};
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const half4_t kd = *reinterpret_cast<const half4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
+      const float4_t kd = *reinterpret_cast<const float4_t*>(&t.kd[b * kStepKeys + 16 * kt + 4 * j]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kt][rt][i] = __builtin_fmaf((float)kd[i], pb[kt][b][rt][i], s[kt][rt][i]);
+        for (int i = 0; i < 4; ++i) s[kt][rt][i] = __builtin_fmaf(kd[i], pb[kt][b][rt][i], s[kt][rt][i]);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -869,30 +879,47 @@ __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int
           if (key > cw.limit[rt] || key >= kend) s[kt][rt][i] = -INFINITY;
         }
   }
+  // Rescale only when a row's max grows by more than 2^kRescaleSlack (also
+  // for a row's first visible keys): s is relative to the stale max, so the
+  // test is s > slack.  A row's max passes only if one of its lanes' values
+  // does: the lane-swap reductions and the rescale run only then (rarely after
+  // the first steps), and shift that row's s to the new max.
+  float lmx[2], thr[2];
+  bool over = false;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    lmx[rt] = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                    fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
+    thr[rt] = cw.m[rt] == -INFINITY ? -INFINITY : kRescaleSlack;
+    over |= lmx[rt] > thr[rt];
+  }
+  if (__any(over)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float mx = max_xor32(max_xor16(lmx[rt]));
+      const bool grow = mx > thr[rt];
+      if (__any(grow)) {
+        const bool fresh = cw.m[rt] == -INFINITY;
+        // 0 for a row's first keys (O and l are still 0); 1 for rows whose max stands
+        const float alpha = grow ? (fresh ? 0.f : __builtin_amdgcn_exp2f(-mx)) : 1.f;
+        const float shift = grow ? mx : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt) cw.o[rt][dt] *= alpha;
+        cw.l[rt] *= alpha;
+        if (grow) cw.m[rt] = (fresh ? 0.f : cw.m[rt]) + mx;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[kt][rt] -= shift;
+      }
+    }
+  }
   half8_t pf[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
-                     fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
-    mx = max_xor32(max_xor16(mx));
-    // rescale only when the max grows by more than 2^kRescaleSlack in exp2 units
-    const bool grow = mx * c > cw.m[rt] * c + kRescaleSlack;  // also true for the first visible keys
-    if (__any(grow)) {
-      const float m_new = grow ? mx : cw.m[rt];
-      // 0 while m is -inf; 1 for rows whose max stands (even a row with no key yet)
-      const float alpha = grow ? __builtin_amdgcn_exp2f((cw.m[rt] - m_new) * c) : 1.f;
-#pragma unroll
-      for (int dt = 0; dt < 2 * NB; ++dt) cw.o[rt][dt] *= alpha;
-      cw.l[rt] *= alpha;
-      cw.m[rt] = m_new;
-    }
-    const float mc = cw.m[rt] == -INFINITY ? 0.f : cw.m[rt] * c;  // rows with nothing visible yet
     float p[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][rt][i], c, -mc));  // <= 2^slack; masked 0
+      for (int i = 0; i < 4; ++i) p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][rt][i]);  // <= 2^slack; masked 0
     pf[rt] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
                      (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
     // the row sums of the fp16 P that the PV products use, on the matrix cores
@@ -1177,7 +1204,7 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
 // output; otherwise its partial goes to slot pslot.  DBG: check page ids
 // (debug mode; a separate instantiation keeps the checks out of the normal
 // step loop).
-template <int NB, int KF, int VF, bool DBG>
+template <int NB, int KF, int VF, bool DBG, bool UNIFORM>
 __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCtx& ic, int r0, int q_len, int prefix,
                                   int g, int hp, int qt, int kb, int ke, int64_t pslot) {
   // every argument is the same across the work-group; say so, so that the
@@ -1204,6 +1231,10 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   chunk_wave_init<NB, KF>(cw, a.q + ((int64_t)(r0 + row0) * a.hq + g * G + hl) * D, a.hq, nrows, prefix + row0,
                           lane);
   const int nst = ceil_div(ke - kb, kStepKeys);
+  // Q is in registers before the step loop starts: the loads still pending
+  // inside the loop are then only the step prefetches, and no product of the
+  // loop waits for them
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // This thread's dequant unit: key tid%32 of one block of K or V.  Each wave
   // holds two units whose blocks have the same parity, hence the same byte
@@ -1226,15 +1257,17 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   ChunkRaw raw;
   auto dequant = [&](int st) {
     const bool valid = kb + st * kStepKeys + u_key < ke;
-    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
-    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid);
+    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid, a.c);
+    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid, a.c);
   };
   // The loads of a step.  Page sizes that are a multiple of 32 keep every step
   // (which starts at a multiple of 32) inside one page: a wave-uniform page
   // walk (scalar page ids, the next page's id fetched a page ahead) and a
   // fixed per-lane offset.  Lanes past the range read bytes of the same page
   // and are zeroed by their scale.  Other page sizes take a per-lane walk.
-  const bool uniform = ps % kStepKeys == 0;
+  // (a separate instantiation per walk: a load pending on one walk's path
+  // must not make the other wait for its own prefetches)
+  constexpr bool uniform = UNIFORM;
   const uint32_t lane_off = (uint32_t)(u_key * rec + (boff & ~3));
   int u_q = kb / ps, u_r = kb % ps;  // page index and slot of the next step to load
   const int q_last = (ke - 1) / ps;
@@ -1286,7 +1319,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     p_page = advance(p_page);
   };
   auto issue = [&](int st) {  // loads of step st (issued in step order)
-    if (uniform) {
+    if constexpr (uniform) {
       issue_uniform();
     } else {
       raw_slot = next_slot;
@@ -1295,7 +1328,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     }
   };
   if (has_unit && nst > 0) {
-    if (uniform) {
+    if constexpr (uniform) {
       u_pg = clamp_page(bt_const[u_q], a.num_pages, DBG, bad_page);
       u_pg_next = u_q < q_last ? clamp_page(bt_const[u_q + 1], a.num_pages, DBG, bad_page) : 0;
     } else {
@@ -1334,7 +1367,7 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     } else {
       const int64_t pi = (pslot * H + hh) * R + row_in_tile;
       dst = a.ch_o + pi * D;
-      if (j == 0) a.ch_ml[pi] = make_float2(cw.m[rt] == -INFINITY ? -INFINITY : cw.m[rt] * a.c, ltot);
+      if (j == 0) a.ch_ml[pi] = make_float2(cw.m[rt], ltot);
     }
 #pragma unroll
     for (int dt = 0; dt < 2 * NB; ++dt) {
@@ -1372,13 +1405,15 @@ __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   ic.page_size = a.page_size;
   const int tile_end = prefix + min(q_len, (qt + 1) * R);  // keys past the tile's last row are never seen
   if (F == 1) {
-    chunk_item<NB, KF, VF, DBG>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
+    if (a.page_size % kStepKeys == 0) chunk_item<NB, KF, VF, DBG, true>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
+    else chunk_item<NB, KF, VF, DBG, false>(a, smem, ic, r0, q_len, prefix, g, hp, qt, 0, tile_end, -1);
     return;
   }
   const int len = ceil_div(ceil_div(tile_end, F), kStepKeys) * kStepKeys;
   const int kb = min(j * len, tile_end), ke = min(kb + len, tile_end);
   if (kb < ke) {
-    chunk_item<NB, KF, VF, DBG>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
+    if (a.page_size % kStepKeys == 0) chunk_item<NB, KF, VF, DBG, true>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
+    else chunk_item<NB, KF, VF, DBG, false>(a, smem, ic, r0, q_len, prefix, g, hp, qt, kb, ke, item);
   } else {  // an empty split: a neutral partial (no keys) for every row of the tile
     const int64_t base = (int64_t)item * H * R;
     for (int u = threadIdx.x; u < H * R; u += blockDim.x) a.ch_ml[base + u] = make_float2(-INFINITY, 0.f);
