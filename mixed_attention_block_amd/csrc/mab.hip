@@ -667,12 +667,13 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
 
 // ---------------------------------------------------------------------------
 // Chunk path.  Every 32-key step is dequantized once into a shared LDS tile
-// (K as exact integer codes with fp32 block scales, V as fp16 values, both
-// [key][dim]); tiles are double buffered.  Each wave serves one query head and
-// 32 rows as two 16-row tiles of 16x16x32 MFMAs: S^T = K Q^T per 32-dim block
-// on integer codes, scaled per key in fp32, then O^T += V^T P^T with the V^T
+// (K as exact integer codes with fp32 block scales times sm_scale*log2(e), V
+// as fp16 values, both [key][dim]); tiles are double buffered.  Each wave
+// serves one query head and 32 rows as two 16-row tiles of 16x16x32 MFMAs:
+// S^T = K Q^T per 32-dim block on integer codes, scaled per key in fp32 and
+// taken relative to the row's running max, then O^T += V^T P^T with the V^T
 // operand read by LDS transpose reads.  A step: dequantize step s+1 from
-// registers into the other tile, issue the global loads of step s+2, compute
+// registers into the other tile, issue the global loads of step s+3, compute
 // step s, one barrier.
 // ---------------------------------------------------------------------------
 
@@ -696,12 +697,22 @@ __device__ inline int value_of_slot(int p) {
 
 // The raw bytes of one dequant unit (the scale and 32 codes of one block of
 // one key of K or V), loaded as dwords from the 4-byte-aligned address at or
-// below the block (the block starts at byte 0 or 2 of w).
+// below the block (the block starts at byte 0 or 2 of w).  The dwords of a
+// 4-bit block sit where those of an 8-bit block do (its last one in w[8]),
+// so that a wave's K and V units of different formats fill the same
+// registers and the array never needs dynamic indexing.
 struct ChunkRaw {
   uint32_t w[16];  // 9 dwords of a quantized block, the 16 of an f16 block
 };
 
+// Register holding dword i of a unit of format F.
 template <int F>
+__device__ constexpr int raw_slot(int i) { return F == MAB_KV_Q4 && i == 4 ? 8 : i; }
+
+// WIDE: the other side (K or V) of the kernel uses 8-bit blocks; a 4-bit
+// unit then takes the same three loads (the second a repeat of the first,
+// unused) so that both sides' loads have one shape.
+template <int F, bool WIDE = false>
 __device__ inline void chunk_raw_load_al(ChunkRaw& r, const uint32_t* base) {
   if constexpr (F == MAB_KV_F16) {  // 64-byte blocks: always 16-byte aligned
 #pragma unroll
@@ -718,37 +729,41 @@ __device__ inline void chunk_raw_load_al(ChunkRaw& r, const uint32_t* base) {
   } else {
     const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base);
     r.w[0] = x0[0]; r.w[1] = x0[1]; r.w[2] = x0[2]; r.w[3] = x0[3];
-    r.w[4] = base[4];
+    if constexpr (WIDE) {
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base);
+      r.w[4] = x1[0]; r.w[5] = x1[1]; r.w[6] = x1[2]; r.w[7] = x1[3];
+    }
+    r.w[raw_slot<F>(4)] = base[4];
   }
 }
 
-template <int F>
+template <int F, bool WIDE = false>
 __device__ inline void chunk_raw_load(ChunkRaw& r, const uint8_t* blk) {
   const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
-  chunk_raw_load_al<F>(r, reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3));
+  chunk_raw_load_al<F, WIDE>(r, reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3));
 }
 
 // Dword m of the unit's codes (codes 4m .. 4m+3, or nibbles 8m .. 8m+7) and
 // the unit's fp16 scale bits.  The block starts at byte SH (0 or 2) of w, so
 // its codes start at byte 2 or 4.
-template <int SH>
+template <int F, int SH>
 __device__ inline uint32_t raw_codes(const ChunkRaw& r, int m) {
-  return SH ? r.w[m + 1] : __builtin_amdgcn_alignbyte(r.w[m + 1], r.w[m], 2);
+  const uint32_t hi = r.w[raw_slot<F>(m + 1)];
+  return SH ? hi : __builtin_amdgcn_alignbyte(hi, r.w[raw_slot<F>(m)], 2);
 }
 template <int SH>
 __device__ inline uint32_t raw_scale(const ChunkRaw& r) { return SH ? r.w[0] >> 16 : r.w[0] & 0xFFFFu; }
 
-// Writes unit (key, block b) of K (is_v false) or V into tile t.  A key past
-// the range (its bytes come from a valid key) gets scale 0: K logits and V
-// values of 0, never a stray NaN.
-template <int NB, int KF, int VF, int SH>
-__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, bool is_v, int key, int b, bool valid,
-                                        float c) {
+// Writes unit (key, block b) of K (IS_V false) or V, in format F, into tile
+// t.  A key past the range (its bytes come from a valid key) gets scale 0: K
+// logits and V values of 0, never a stray NaN.  c = sm_scale*log2(e) is
+// folded into the K scale.
+template <int NB, int F, bool IS_V, int SH>
+__device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, int key, int b, bool valid, float c) {
   using T = ChunkTile<NB>;
-  const int F = is_v ? VF : KF;
   half_t d;
   half8_t out[4];
-  if (F == MAB_KV_F16) {  // the values themselves, scale 1
+  if constexpr (F == MAB_KV_F16) {  // the values themselves, scale 1
     d = (half_t)1.f;
     // a key past the range holds whatever the pool holds there (possibly
     // NaN): zero its values, as a scale of 0 does for the quantized formats
@@ -761,13 +776,13 @@ __device__ inline void chunk_unit_store(ChunkTile<NB>& t, const ChunkRaw& r, boo
     d = __builtin_bit_cast(half_t, (uint16_t)raw_scale<SH>(r));
 #pragma unroll
     for (int g8 = 0; g8 < 4; ++g8) {
-      if (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes<SH>(r, 2 * g8), raw_codes<SH>(r, 2 * g8 + 1));
-      else out[g8] = codes8_q4(raw_codes<SH>(r, g8));
+      if constexpr (F == MAB_KV_Q8) out[g8] = codes8_q8(raw_codes<F, SH>(r, 2 * g8), raw_codes<F, SH>(r, 2 * g8 + 1));
+      else out[g8] = codes8_q4(raw_codes<F, SH>(r, g8));
     }
   }
   if (!valid) d = (half_t)0.f;
-  half_t* row = (is_v ? t.v : t.k) + key * T::kStride + 32 * b;
-  if (is_v) {
+  half_t* row = (IS_V ? t.v : t.k) + key * T::kStride + 32 * b;
+  if constexpr (IS_V) {
     const half8_t dv = half8_t{d, d, d, d, d, d, d, d};
 #pragma unroll
     for (int g8 = 0; g8 < 4; ++g8) *reinterpret_cast<half8_t*>(row + 8 * g8) = out[g8] * dv;
@@ -820,13 +835,13 @@ __device__ inline void chunk_wave_init(ChunkWave<NB>& cw, const half_t* q0, int 
 }
 
 // One 32-key step of a wave on tile t (keys kbase .. kbase+31, those at or
-// past kend zeroed).  Logits S stay in raw units (sum of block scale times the
-// integer-code dot product); c = sm_scale*log2(e) > 0 is applied inside the
-// exponent, so the running max m is in raw units too.  `masked`: some key of
-// the step lies past a row's limit or past kend.
+// past kend zeroed).  Logits are in exp2 units (the block scales in the tile
+// already carry c = sm_scale*log2(e)) and relative to the row's running max m,
+// so P = exp2(S).  `masked`: some key of the step lies past a row's limit or
+// past kend.
 template <int NB>
 __device__ inline void chunk_step(ChunkWave<NB>& cw, const ChunkTile<NB>& t, int kbase, int kend, bool masked,
-                                  float c, int lane) {
+                                  int lane) {
   using T = ChunkTile<NB>;
   const int n = lane & 15, j = lane >> 4;
   float4_t s[2][2];  // [key tile][row tile]
@@ -1254,11 +1269,18 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   // byte offset of the unit's block in its dword (the same for every lane of a
   // wave: records are a multiple of 4 bytes, pools 16-byte aligned)
   const int sh = __builtin_amdgcn_readfirstlane(boff & 3);
-  ChunkRaw raw;
-  auto dequant = [&](int st) {
+  ChunkRaw raw_a, raw_b;  // the loads of two steps in flight: even steps in raw_a, odd ones in raw_b
+  constexpr bool kWide = KF == MAB_KV_Q8 || VF == MAB_KV_Q8;
+  auto dequant = [&](int st, const ChunkRaw& raw) {
     const bool valid = kb + st * kStepKeys + u_key < ke;
-    if (sh) chunk_unit_store<NB, KF, VF, 2>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid, a.c);
-    else chunk_unit_store<NB, KF, VF, 0>(tiles[st & 1], raw, u_is_v, u_key, u_b, valid, a.c);
+    ChunkTile<NB>& t = tiles[st & 1];
+    if (u_is_v) {
+      if (sh) chunk_unit_store<NB, VF, true, 2>(t, raw, u_key, u_b, valid, a.c);
+      else chunk_unit_store<NB, VF, true, 0>(t, raw, u_key, u_b, valid, a.c);
+    } else {
+      if (sh) chunk_unit_store<NB, KF, false, 2>(t, raw, u_key, u_b, valid, a.c);
+      else chunk_unit_store<NB, KF, false, 0>(t, raw, u_key, u_b, valid, a.c);
+    }
   };
   // The loads of a step.  Page sizes that are a multiple of 32 keep every step
   // (which starts at a multiple of 32) inside one page: a wave-uniform page
@@ -1275,10 +1297,10 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
   const __attribute__((address_space(4))) int32_t* bt_const =
       (const __attribute__((address_space(4))) int32_t*)(wave_uniform(ic.bt_row));
   int u_pg = 0, u_pg_next = 0, bad_page = 0;
-  auto issue_uniform = [&]() {
+  auto issue_uniform = [&](ChunkRaw& raw) {
     const uint8_t* base = pool + (((int64_t)u_pg * ic.hkv + g) * ps + u_r) * rec;
-    if (u_is_v) chunk_raw_load_al<VF>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
-    else chunk_raw_load_al<KF>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
+    if (u_is_v) chunk_raw_load_al<VF, kWide>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
+    else chunk_raw_load_al<KF, kWide>(raw, reinterpret_cast<const uint32_t*>(base + lane_off));
     u_r += kStepKeys;
     if (u_r == ps) {
       u_r = 0;
@@ -1303,14 +1325,14 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     slot = t - c * ps;
   };
   int raw_slot = 0;
-  auto issue_lane = [&](int page) {  // the unit's own block only: the read never leaves the key's record
+  auto issue_lane = [&](ChunkRaw& raw, int page) {  // the unit's own block only: the read never leaves the key's record
     const int64_t tok = ((int64_t)page * ic.hkv + g) * ps + raw_slot;
-    if (u_is_v) chunk_raw_load<VF>(raw, pool + tok * rec + boff);
-    else chunk_raw_load<KF>(raw, pool + tok * rec + boff);
+    if (u_is_v) chunk_raw_load<VF, kWide>(raw, pool + tok * rec + boff);
+    else chunk_raw_load<KF, kWide>(raw, pool + tok * rec + boff);
   };
   // pipeline: the tile of step st+1 is filled from registers during step st,
-  // whose loads were issued during step st-1 (per-lane walk: with page ids
-  // fetched during st-2)
+  // whose loads were issued during step st-2 (per-lane walk: with page ids
+  // fetched one issue earlier); two register sets hold the loads in flight
   Pos p_page = {kb / ps, kb % ps};  // step of the next page-id fetch
   int pidx, next_slot = 0, pg_next = 0;
   auto fetch_page = [&](int st) {
@@ -1318,12 +1340,12 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     pg_next = clamp_page(ic.bt_row[pidx], a.num_pages, DBG, bad_page);
     p_page = advance(p_page);
   };
-  auto issue = [&](int st) {  // loads of step st (issued in step order)
+  auto issue = [&](int st, ChunkRaw& raw) {  // loads of step st (issued in step order)
     if constexpr (uniform) {
-      issue_uniform();
+      issue_uniform(raw);
     } else {
       raw_slot = next_slot;
-      issue_lane(pg_next);
+      issue_lane(raw, pg_next);
       if (st + 1 < nst) fetch_page(st + 1);
     }
   };
@@ -1334,21 +1356,29 @@ __device__ inline void chunk_item(const AttnArgs& a, uint8_t* smem, const ItemCt
     } else {
       fetch_page(0);
     }
-    issue(0);
-    dequant(0);
-    if (nst > 1) issue(1);
+    issue(0, raw_a);
+    if (nst > 1) issue(1, raw_b);
+    dequant(0, raw_a);
+    if (nst > 2) issue(2, raw_a);
   }
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
+  // step st: the tile of step st+1 is filled from the set holding it (raw_b
+  // for even st), whose loads were issued two steps earlier, and the set is
+  // reloaded with step st+3
+  auto body = [&](int st, ChunkRaw& raw) {
     const int kbase = kb + st * kStepKeys;
     if (has_unit && st + 1 < nst) {
-      dequant(st + 1);
-      if (st + 2 < nst) issue(st + 2);
+      dequant(st + 1, raw);
+      if (st + 3 < nst) issue(st + 3, raw);
     }
     // every wave computes (one past the last row on zero queries, written nowhere)
     const bool masked = kbase + kStepKeys - 1 > prefix + row0 || kbase + kStepKeys > ke;
-    chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, a.c, lane);
+    chunk_step<NB>(cw, tiles[st & 1], kbase, ke, masked, lane);
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    body(st, raw_b);
+    if (st + 1 < nst) body(st + 1, raw_a);
   }
   report_bad_page(bad_page);
   if (nrows == 0) return;

@@ -1,7 +1,8 @@
 """GPU parity at the benchmark workloads' full sizes, in the launch
 configuration bench.py times.  The whole batch runs on the GPU; the oracle
-recomputes a sample of rows (decode rows incl. the longest, and chunk rows at
-tile and split boundaries) and the KV bytes of the sampled sequences' pages."""
+recomputes every decode and verify row, the chunk rows at every 128-row tile
+edge, and the KV bytes of every page the batch uses.  The 12-layer full step
+is checked layer by layer (each layer has its own values)."""
 
 import sys
 
@@ -16,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 WORKLOADS = [("decode16", 2), ("decode16_f16", 2), ("verify16", 6), ("mixed16_chunk2k", 3), ("long_q8", 4),
              ("long_k4v4", 4), ("step_k4v4", 5)]
+STEP_LAYERS = 12  # the full step: layer l draws its values with value_seed 100 * seed + l
 
 
 def _say(msg):
@@ -24,22 +26,22 @@ def _say(msg):
 
 
 def _sample(case):
+    """Every row of every sequence of at most 16 rows (decode and verify rows),
+    and for each prefill chunk the first and last row of every 128-row tile
+    (the chunk tiles hold 128 rows of two query heads at 24/4 heads) plus
+    rows next to them and in the middle of the chunk."""
     seqs, rows = [], []
-    dec = [s for s in range(case.num_seqs) if case.q_len(s) == 1]
-    if dec:
-        longest = max(dec, key=case.context)
-        shortest = min(dec, key=case.context)
-        for s in dict.fromkeys([longest, shortest, dec[len(dec) // 2]]):
-            seqs.append(s)
-            rows.append(int(case.q_start[s]))
     for s in range(case.num_seqs):
         n = case.q_len(s)
-        if n > 1:
-            seqs.append(s)
-            r0 = int(case.q_start[s])
-            for i in sorted({0, 1, 31, 32, 33, n // 2, n - 33, n - 2, n - 1}):
-                if 0 <= i < n:
-                    rows.append(r0 + i)
+        r0 = int(case.q_start[s])
+        seqs.append(s)
+        if n <= 16:
+            rows.extend(range(r0, r0 + n))
+            continue
+        picks = {1, 33, n // 2, n - 2}
+        for t0 in range(0, n, 128):
+            picks.update({t0, t0 + 127})
+        rows.extend(r0 + i for i in sorted(picks) if 0 <= i < n)
     return seqs, rows
 
 
@@ -72,4 +74,35 @@ def test_fullsize_sampled(name, seed):
     want = oracle_out(case, kp, vp, rows=rows)
     got = out.cpu().numpy()
     mx, mean = assert_close(got[rows], want[rows], name)
+    _say(f"  max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("layer", range(1, STEP_LAYERS))
+def test_fullsize_step_layer(layer):
+    """Layers 1-11 of the 12-layer full step (layer 0 is the step_k4v4 case
+    above, every row): the chunk rows at the first and last 128-row tile
+    edges and three decode rows (the two shortest, the longest), against the
+    oracle, with the KV bytes of their pages."""
+    seed = 5
+    _say(f"fullsize step_k4v4 layer={layer}: building on GPU")
+    case = synth.make_case("step_k4v4", seed, device="cuda", value_seed=seed * 100 + layer)
+    st = GpuState(case)
+    st.append_step()
+    out = st.attention()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "non-finite output"
+    chunk = next(s for s in range(case.num_seqs) if case.q_len(s) > 16)
+    c0, n = int(case.q_start[chunk]), case.q_len(chunk)
+    dec = sorted((s for s in range(case.num_seqs) if case.q_len(s) == 1), key=case.context)
+    picked = [dec[0], dec[1], dec[-1]]  # the two shortest rows and the longest
+    rows = [c0, c0 + 127, c0 + n - 128, c0 + n - 1] + [int(case.q_start[s]) for s in picked]
+    seqs = [chunk] + picked
+    _say(f"  oracle on {len(rows)} rows")
+    kp, vp = oracle_pools(case, seqs=seqs)
+    gk, gv = st.pools_host()
+    pages = _pages_of(case, seqs)
+    assert np.array_equal(gk[pages], kp[pages]), "K bytes differ"
+    assert np.array_equal(gv[pages], vp[pages]), "V bytes differ"
+    want = oracle_out(case, kp, vp, rows=rows)
+    mx, mean = assert_close(out.cpu().numpy()[rows], want[rows], f"step_k4v4 layer {layer}")
     _say(f"  max abs {mx:.2e} mean abs {mean:.2e}")

@@ -216,8 +216,9 @@ def _sweep_values(gen, n, hkv, d, kind):
 
 @pytest.mark.parametrize("fmt", ["q8", "q4"])
 def test_append_random_sweep(fmt):
-    """~1.6M blocks of mixed distributions, bit-exact against the oracle."""
-    n, hkv, d = 8192, 4, 128
+    """11M blocks per format (K and V, seven distributions of 49152 rows x 4
+    heads x 4 blocks each), bit-exact against the oracle."""
+    n, hkv, d = 49152, 4, 128
     kinds = ["normal", "outliers", "subnormal_scales", "underflow", "ties", "wide", "sparse"]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(77)
