@@ -264,10 +264,12 @@ int64_t mab_probe_mfma_f16(int32_t iters, void* sink, void* stream);
  *  - Served decoders move to the back of the queue (PopDecoder rotation).
  *    After a merged step every resident decoder is due
  *    (MarkAllDecodersDue).
- *  - The chunk goes to the earliest request with at most one chunk left,
- *    else to the earliest other prefill (SRTF).  While a request waits for a
- *    slot and some decoder is within near_done_gate tokens of its limit,
- *    prefills with more than one chunk left get no chunk.
+ *  - The chunk goes to the prefill that needs the fewest chunk slices to
+ *    finish, ceil(remaining / prefill_chunk), the earliest request among
+ *    equal counts (SRTF): a prefill with one slice left goes before every
+ *    longer one.  While a request waits for a slot and some decoder is within
+ *    near_done_gate tokens of its limit, prefills with more than one slice
+ *    left get no chunk.
  *
  * Positions: a chunk row covers prompt positions [prefix, prefix + q_len).
  * A decoder that has produced g tokens feeds token g: one row with

@@ -21,10 +21,13 @@
 //  * Served decoders move to the back of the decode queue, in their order
 //    (PopDecoder rotation).  After a merged step every resident decoder is
 //    due (MarkAllDecodersDue).
-//  * Chunk choice.  A prefill with at most one chunk left goes first (SRTF),
-//    earliest request first within a class.  While a request waits for a
-//    slot, prefills with more than one chunk left get no chunk if some
-//    resident decoder is within near_done_gate tokens of its limit.
+//  * Chunk choice (SRTF).  Prefills are ordered by the chunk slices they
+//    still need, fewest first, earliest request first within a count: one
+//    with a single slice left ("near done") goes before every longer one,
+//    and a short prompt before a long prompt's continuation slices.  While a
+//    request waits for a slot, prefills with more than one slice left get
+//    no chunk if some resident decoder is within near_done_gate tokens of
+//    its limit.
 //
 // The state is plain arrays indexed by request id, with a min-heap of free
 // pages.  A tick costs O(resident + decoders + rows * max_pages_per_seq).
@@ -99,18 +102,18 @@ struct mab_sched {
     if (n_pending > 0)
       for (int64_t d : queue)
         if (req[d].limit - req[d].generated <= cfg.near_done_gate) starving = true;
-    int64_t near = -1, far = -1;
+    int64_t best = -1, best_slices = 0;
     for (int64_t id : resident) {
       const Req& r = req[id];
       if (r.phase != kPrefill) continue;
-      if (r.prompt - r.prefilled <= cfg.prefill_chunk) {
-        if (near < 0 || id < near) near = id;
-      } else if (far < 0 || id < far) {
-        far = id;
+      const int64_t slices = ((int64_t)r.prompt - r.prefilled + cfg.prefill_chunk - 1) / cfg.prefill_chunk;
+      if (best < 0 || slices < best_slices || (slices == best_slices && id < best)) {
+        best = id;
+        best_slices = slices;
       }
     }
-    if (near >= 0) return near;
-    return starving ? -1 : far;
+    if (best >= 0 && best_slices > 1 && starving) return -1;  // only a near-done prefill may run
+    return best;
   }
 
   void release(int64_t id) {

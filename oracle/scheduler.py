@@ -35,9 +35,12 @@ R-S4  PopDecoder rotation: the decoders a step serves move to the back of
 R-S5  MarkAllDecodersDue: after a merged step, every resident decoder is due,
       including one whose prefill finished in that step.  A decode step
       clears the flag of the decoders it served.
-R-S6  SRTF: a prefill with at most one chunk left (remaining <= prefill_chunk)
-      is "near done".  Near-done prefills go before the others.  Within a
-      class, the earlier request goes first.
+R-S6  SRTF: prefills are ordered by the chunk slices they still need,
+      ceil(remaining / prefill_chunk), fewest first; within a class (the same
+      count) the earlier request goes first.  A prefill with one slice left
+      (remaining <= prefill_chunk) is "near done" and so goes before every
+      longer prefill continuation, and a prompt of a few slices goes before a
+      long prompt's continuation slices.
 R-S7  Starving-decode preemption with the near-done gate: while some request
       is pending, and some resident decoder has at most near_done_gate tokens
       left, prefills that are not near done get no chunk.
@@ -133,12 +136,15 @@ class Scheduler:
             if self.pending[client]:
                 self.rotation.append(client)
 
+    def slices_left(self, r):
+        return -(-(r.prompt - r.prefilled) // self.chunk)
+
     def pick_chunk(self):
-        prefills = sorted((r for r in self.resident if r.state == "prefill"), key=lambda r: r.rid)
-        near = [r for r in prefills if r.prompt - r.prefilled <= self.chunk]
-        far = [r for r in prefills if r.prompt - r.prefilled > self.chunk]
+        prefills = sorted((r for r in self.resident if r.state == "prefill"),
+                          key=lambda r: (self.slices_left(r), r.rid))
+        near = [r for r in prefills if self.slices_left(r) == 1]
         starving = self.any_pending() and any(r.limit - r.generated <= self.gate for r in self.decode_queue)
-        choices = near if starving else near + far
+        choices = near if starving else prefills
         return choices[0] if choices else None
 
     def step(self):

@@ -117,10 +117,21 @@ class _FifoPrefill(sched.Scheduler):
 
 class _NoGate(sched.Scheduler):
     def pick_chunk(self):
+        prefills = sorted((r for r in self.resident if r.state == "prefill"),
+                          key=lambda r: (self.slices_left(r), r.rid))
+        return prefills[0] if prefills else None
+
+
+class _TwoClassSrtf(sched.Scheduler):
+    """Near done first, then first come first served among the others."""
+
+    def pick_chunk(self):
         prefills = sorted((r for r in self.resident if r.state == "prefill"), key=lambda r: r.rid)
         near = [r for r in prefills if r.prompt - r.prefilled <= self.chunk]
         far = [r for r in prefills if r.prompt - r.prefilled > self.chunk]
-        return (near + far)[0] if prefills else None
+        starving = self.any_pending() and any(r.limit - r.generated <= self.gate for r in self.decode_queue)
+        choices = near if starving else near + far
+        return choices[0] if choices else None
 
 
 class _NoRotation(sched.Scheduler):
@@ -182,7 +193,7 @@ def _scheduler_pins(make):
         obs.check_admission_rotation()
 
 
-@pytest.mark.parametrize("mutant", [_NoMarkAllDue, _FifoPrefill, _NoGate, _NoRotation, _ChunkFirst,
+@pytest.mark.parametrize("mutant", [_NoMarkAllDue, _FifoPrefill, _NoGate, _TwoClassSrtf, _NoRotation, _ChunkFirst,
                                     _GlobalFifoAdmission, _DecodePrefixOffByOne], ids=lambda m: m.__name__)
 def test_scheduler_mutants_are_caught(mutant):
     with pytest.raises(AssertionError):

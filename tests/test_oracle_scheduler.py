@@ -125,6 +125,8 @@ class Observer:
         rem = {rid: self.info[rid][1] - self.prefilled[rid] for rid in prefills}
         near = [rid for rid in prefills if rem[rid] <= cfg["prefill_chunk"]]
         far = [rid for rid in prefills if rem[rid] > cfg["prefill_chunk"]]
+        # fewest slices left first, the earlier request within a count
+        far.sort(key=lambda rid: (-(-rem[rid] // cfg["prefill_chunk"]), rid))
         decoders = [rid for rid in self.generated if self.is_decoder(rid)]
         starving = self.pre_pending and any(self.info[d][2] - self.generated[d] <= cfg["near_done_gate"]
                                            for d in decoders)
@@ -134,7 +136,7 @@ class Observer:
             assert chunk_rid == near[0], "SRTF: the earliest near-done prefill goes first"
         else:
             assert not starving, "a far prefill ran while a waiting request starved"
-            assert chunk_rid == far[0], "FIFO among far prefills"
+            assert chunk_rid == far[0], "SRTF among longer prefills (fewest slices left, then FIFO)"
 
     def is_decoder(self, rid):
         return (rid not in self.finished and self.prefilled[rid] == self.info[rid][1]
