@@ -58,9 +58,10 @@ POISON = 0x7E  # bytes of pool space no append has written (fp16 NaN scales)
 class DeviceCase:
     """One layer's device state: pools written by kv_append_quant (the cached
     prefix first, then the step's rows at their own positions), the batch
-    descriptor, the step's inputs, an output buffer and the workspace."""
+    descriptor, the step's inputs, an output buffer and the workspace.
+    ``flags``: the attention batch's flags (0, or MAB_BATCH_INVARIANT)."""
 
-    def __init__(self, case):
+    def __init__(self, case, flags=0):
         import torch
         import mixed_attention_block_amd as mab
 
@@ -72,7 +73,7 @@ class DeviceCase:
                                  dtype=torch.uint8, device="cuda")
         self.v_pool = torch.full((mab.kv_pool_bytes(self.layout, lay["v_format"]),), POISON,
                                  dtype=torch.uint8, device="cuda")
-        self.batch = self._batch(case.q_start, case.prefix_len, case.block_table)
+        self.batch = self._batch(case.q_start, case.prefix_len, case.block_table, flags)
         # the cached prefix: one append over every sequence that has one
         keep = [s for s in range(case.num_seqs) if case.prefix_len[s] > 0]
         if keep:
@@ -93,7 +94,7 @@ class DeviceCase:
         self.ws = torch.empty((max(n, 256),), dtype=torch.uint8, device="cuda")
 
     @staticmethod
-    def _batch(q_start, prefix_len, block_table):
+    def _batch(q_start, prefix_len, block_table, flags=0):
         import torch
         import mixed_attention_block_amd as mab
 
@@ -101,7 +102,7 @@ class DeviceCase:
         pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
         bt = np.ascontiguousarray(block_table, dtype=np.int32)
         return mab.BatchDesc(torch.from_numpy(qs).cuda(), torch.from_numpy(pl).cuda(),
-                             torch.from_numpy(bt).cuda(), qs, pl)
+                             torch.from_numpy(bt).cuda(), qs, pl, flags=flags)
 
 
 def realism_probes(stream):
@@ -319,6 +320,8 @@ def main():
     ap.add_argument("--workload", default="step_k4v4", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch-invariant", action="store_true",
+                    help="attention batches with MAB_BATCH_INVARIANT (decode rows cut from their own first key)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -345,7 +348,7 @@ def main():
     for layer in range(layers):
         case = synth.make_case(name, seed, device="cuda",
                                value_seed=seed * 100 + layer if layers > 1 else None)
-        st = DeviceCase(case)
+        st = DeviceCase(case, mab.MAB_BATCH_INVARIANT if args.batch_invariant else 0)
         bpp = kv_bytes_per_position(case.layout)
         kv_bytes += sum(case.context(s) for s in range(case.num_seqs)) * bpp
         rows = case.num_rows  # the layers share one batch
@@ -446,6 +449,7 @@ def main():
             "kv_bytes_per_step": int(kv_bytes),
             "kv_format": f"K{first_case.layout['k_format']}/V{first_case.layout['v_format']}",
             "pool_copies_rotated": copies,
+            "batch_invariant": bool(args.batch_invariant),
         },
         "query_tok_s": round(rows / (ms_per_step * 1e-3), 1),
         "attention_ms_avg": round(attn_avg, 6),

@@ -102,12 +102,30 @@ typedef struct mab_kv_layout {
   int32_t reserved;     /* must be 0                             */
 } mab_kv_layout;
 
+/* Batch flags.
+ *
+ * MAB_BATCH_INVARIANT: every decode and verify row (a sequence of at most 16
+ * rows) gives bit-identical outputs whatever else shares the batch, as the
+ * MBufo page's three-numbers table (greedy output bit-identical) and the
+ * fairness part of its section 1 (a prompt checked by hash alone and under
+ * load) ask of a serving engine.  Without it, the keys of all decode rows are
+ * cut into equal ranges per wave across the whole batch, so a row's split
+ * points, and with them its fp32 rounding (within 1e-3 of the output), depend
+ * on the other rows; with it, each row's keys are cut into pieces of
+ * MAB_INVARIANT_PIECE_KEYS from its own first key and each piece runs on its
+ * own wave.  Prefill-chunk rows are batch-independent either way: their key
+ * splits depend only on their own tile count and the device's compute-unit
+ * count.  Cost on one MI355X: about +30% on a batch of 16 short decode rows,
+ * +15% on 4-token verify rows, nothing on single long rows. */
+enum { MAB_BATCH_INVARIANT = 1 };
+#define MAB_INVARIANT_PIECE_KEYS 512
+
 /* One ForwardBatch: chunk rows and decode rows together (MBufo page, section 1). */
 typedef struct mab_batch {
   int32_t num_seqs;          /* S                                                 */
   int32_t num_rows;          /* total query rows = q_start[S]                     */
   int32_t max_pages_per_seq; /* row stride of block_table                         */
-  int32_t reserved;          /* must be 0                                         */
+  int32_t flags;             /* 0, or MAB_BATCH_INVARIANT                         */
   const int32_t* q_start;         /* device [S+1], q_start[0] = 0, non-decreasing */
   const int32_t* prefix_len;      /* device [S], cached positions before the rows */
   const int32_t* block_table;     /* device [S * max_pages_per_seq] page ids      */

@@ -22,6 +22,8 @@ MAB_KV_Q8 = 1
 MAB_KV_Q4 = 2
 MAB_KV_F16 = 3
 FORMATS = {"q8": MAB_KV_Q8, "q4": MAB_KV_Q4, "f16": MAB_KV_F16}
+MAB_BATCH_INVARIANT = 1  # batch flag: decode and verify rows bit-identical whatever shares the batch
+INVARIANT_PIECE_KEYS = 512  # MAB_INVARIANT_PIECE_KEYS
 
 
 class MabError(RuntimeError):
@@ -39,7 +41,7 @@ class KVLayout(ctypes.Structure):
 
 class Batch(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("q_start", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("q_start_host", ctypes.c_void_p),
                 ("prefix_len_host", ctypes.c_void_p)]
@@ -110,7 +112,7 @@ class BatchDesc:
     ``q_start_host``, ``prefix_len_host``: int32 host arrays with the same values.
     """
 
-    def __init__(self, q_start, prefix_len, block_table, q_start_host, prefix_len_host):
+    def __init__(self, q_start, prefix_len, block_table, q_start_host, prefix_len_host, flags=0):
         self._keep = [q_start, prefix_len, block_table,
                       np.ascontiguousarray(q_start_host, dtype=np.int32),
                       np.ascontiguousarray(prefix_len_host, dtype=np.int32)]
@@ -121,7 +123,7 @@ class BatchDesc:
         if len(qh) != num_seqs + 1:
             raise ValueError("q_start_host must have num_seqs + 1 entries")
         max_pages = block_table.shape[-1] if block_table.dim() == 2 else max(1, block_table.numel())
-        self.struct = Batch(num_seqs, int(qh[-1]) if num_seqs else 0, int(max_pages), 0,
+        self.struct = Batch(num_seqs, int(qh[-1]) if num_seqs else 0, int(max_pages), int(flags),
                             q_start.data_ptr(), prefix_len.data_ptr(), block_table.data_ptr(),
                             qh.ctypes.data, ph.ctypes.data)
 

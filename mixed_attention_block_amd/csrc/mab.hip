@@ -132,6 +132,17 @@ __host__ __device__ inline int chunk_tiles(int q_len, int hkv, int group) {
   return ceil_div(q_len, chunk_rows(group)) * hkv * (group / chunk_heads(group));
 }
 __host__ __device__ inline int dec_stages(int ctx) { return ceil_div(ctx, kStepKeys); }
+// Units a decode segment takes in the decode stream: its stages, or, for
+// batches with MAB_BATCH_INVARIANT (piece = stages per piece), its stages
+// rounded up to whole pieces, so that every segment starts on a piece
+// boundary and the pieces of one range per wave are cut from the segment's
+// own first key.  The padding units hold no work.
+constexpr int kInvariantPiece = MAB_INVARIANT_PIECE_KEYS / kStepKeys;
+static_assert(MAB_INVARIANT_PIECE_KEYS % kStepKeys == 0, "whole stages per invariant piece");
+__host__ __device__ inline int dec_units_of(int ctx, int piece) {
+  const int n = dec_stages(ctx);
+  return piece > 0 ? ceil_div(n, piece) * piece : n;
+}
 
 // Key splits per tile of a chunk sequence: the F in 1..8 whose tiles*F work
 // items fill whole rounds of `slots` resident work-groups best (the smallest
@@ -1024,7 +1035,8 @@ struct AttnArgs {
   int n_dec, n_chunk;       // decode and chunk sequences
   int n_chunk_items;        // chunk work items (the first entries of the grid)
   int ch_target;            // work-group slots the chunk splits aim to fill
-  int dec_units;            // stages in the decode stream
+  int dec_units;            // units in the decode stream (stages, plus padding with dec_piece)
+  int dec_piece;            // 0: equal ranges over the stream; else stages per piece (MAB_BATCH_INVARIANT)
   int dec_range;            // stages per decode worker (the last may have fewer)
   int dec_pmax;             // partial slots per decode worker
   int dec_slots;            // (row, head) slots of a decode partial: G, or T*G with verify rows
@@ -1189,25 +1201,28 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
   int x = x0, k = 0;
   while (x < x1) {
     const int ctx = tv.dec_ctx[e], ub = tv.dec_unit[e], ntok = tv.dec_ntok[e];
-    const int nst = dec_stages(ctx);
+    const int nst = dec_units_of(ctx, a.dec_piece);   // the segment's units in the stream
     const int g = (x - ub) / nst;
     const int seg_lo = ub + g * nst, seg_hi = seg_lo + nst;
+    const int work_hi = seg_lo + dec_stages(ctx);     // units past it are padding
     const int p_hi = min(x1, seg_hi);
-    const int r0 = tv.dec_r0[e];
-    const bool first = x == seg_lo, whole = first && p_hi == seg_hi;
-    const int64_t slot = (int64_t)w * a.dec_pmax + k;
-    decode_piece<NB, KF, VF, DEPTH, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
-                                    min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
-    if (first && (threadIdx.x & 63) == 0) {
-      DirEntry d;
-      d.slot = (int)slot;
-      d.wg = w;
-      d.n = whole ? 1 : (seg_hi - 1) / a.dec_range - w + 1;
-      d.rh0 = r0 * a.hq + g * G;
-      a.dir[e * a.hkv + g] = d;
+    if (x < work_hi) {
+      const int r0 = tv.dec_r0[e];
+      const bool first = x == seg_lo, whole = first && p_hi >= work_hi;
+      const int64_t slot = (int64_t)w * a.dec_pmax + k;
+      decode_piece<NB, KF, VF, DEPTH, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
+                                           min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
+      if (first && (threadIdx.x & 63) == 0) {
+        DirEntry d;
+        d.slot = (int)slot;
+        d.wg = w;
+        d.n = whole ? 1 : (work_hi - 1) / a.dec_range - w + 1;
+        d.rh0 = r0 * a.hq + g * G;
+        a.dir[e * a.hkv + g] = d;
+      }
+      ++k;
     }
     x = p_hi;
-    ++k;
     if (x == seg_hi && g + 1 == a.hkv) ++e;
   }
 }
@@ -1640,7 +1655,7 @@ plan_kernel(AttnArgs a) {
     } else {
       for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
         v[0] += 1;
-        v[1] += a.hkv * dec_stages(ctx - q_len + min(q_len, (i + 1) * T));
+        v[1] += a.hkv * dec_units_of(ctx - q_len + min(q_len, (i + 1) * T), a.dec_piece);
       }
     }
   }
@@ -1681,7 +1696,7 @@ plan_kernel(AttnArgs a) {
         w[t.dec_r0 + e] = r0 + i * T;
         w[t.dec_ctx + e] = prefix + t1;
         w[t.dec_ntok + e] = t1 - i * T;
-        base[1] += a.hkv * dec_stages(prefix + t1);
+        base[1] += a.hkv * dec_units_of(prefix + t1, a.dec_piece);
       }
     }
   }
@@ -1712,6 +1727,7 @@ struct HostPlan {
   int n_dec = 0, n_chunk = 0, n_chunk_items = 0, ch_target = 1;
   bool ch_splits = false;  // some chunk tile is cut into several splits
   int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
+  int dec_piece = 0;       // stages per piece with MAB_BATCH_INVARIANT, else 0
   int dec_seg_pieces = 1;  // pieces of the most cut decode segment
   int dec_slots = 1;       // (row, head) slots per decode partial
   int64_t n_slots = 0;
@@ -1732,7 +1748,9 @@ int device_cus() {
 
 int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   if (!B) return MAB_ERR_NULL;
-  if (B->num_seqs < 0 || B->num_rows < 0 || B->max_pages_per_seq < 1 || B->reserved) return MAB_ERR_SHAPE;
+  if (B->num_seqs < 0 || B->num_rows < 0 || B->max_pages_per_seq < 1 || (B->flags & ~MAB_BATCH_INVARIANT))
+    return MAB_ERR_SHAPE;
+  const int piece = (B->flags & MAB_BATCH_INVARIANT) ? kInvariantPiece : 0;
   if (B->num_seqs > kMaxSeqs) return MAB_ERR_UNSUPPORTED;
   if (B->num_seqs == 0) return B->num_rows == 0 ? MAB_OK : MAB_ERR_SHAPE;
   if (!B->q_start || !B->prefix_len || !B->block_table || !B->q_start_host || !B->prefix_len_host)
@@ -1758,7 +1776,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     } else {
       const int T = dec_tokens(G), nsub = dec_subrows((int)q_len, G);
       for (int i = 0; i < nsub; ++i)
-        units += (int64_t)hkv * dec_stages((int)(prefix + std::min<int64_t>(q_len, (int64_t)(i + 1) * T)));
+        units += (int64_t)hkv * dec_units_of((int)(prefix + std::min<int64_t>(q_len, (int64_t)(i + 1) * T)), piece);
       n_dec += nsub;
       max_ntok = std::max<int>(max_ntok, (int)std::min<int64_t>(q_len, T));
     }
@@ -1771,16 +1789,21 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->ch_target = ch_target;
   hp->ch_splits = ch_splits;
   hp->dec_units = (int)units;
+  hp->dec_piece = piece;
   hp->dec_slots = max_ntok * G;
   if (units > 0) {
     // equal ranges, one per decode worker (a wave), as many as the device
     // holds at once (eight waves per compute unit: two 4-wave work-groups of
     // the decode kernel or one 8-wave work-group of the mixed kernel), fewer
     // for small batches: at least kMinWaveStages stages each
+    // (with MAB_BATCH_INVARIANT: one piece per worker, as many workers as
+    // pieces, the work-groups past the device's capacity dispatched as others
+    // finish)
     const int nw = n_chunk > 0 ? kMixedWaves : kDecodeWaves;
     const int64_t max_workers = (int64_t)8 * cus;
     int64_t workers = std::min<int64_t>(max_workers, std::max<int64_t>(1, units / kMinWaveStages));
-    const int64_t range = ceil_div64(units, workers);
+    int64_t range = ceil_div64(units, workers);
+    if (piece > 0) range = piece;
     workers = ceil_div64(units, range);
     hp->dec_wgs = (int)ceil_div64(workers, nw);
     hp->dec_range = (int)range;
@@ -1791,10 +1814,11 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
       const int q_len = B->q_start_host[s + 1] - B->q_start_host[s];
       if (is_chunk(q_len)) continue;
       for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
-      const int nst = dec_stages(B->prefix_len_host[s] + std::min(q_len, (i + 1) * T));
+      const int ctx = B->prefix_len_host[s] + std::min(q_len, (i + 1) * T);
+      const int nst = dec_units_of(ctx, piece), nwork = dec_stages(ctx);
       for (int g = 0; g < hkv; ++g, x += nst) {
         if (x % range != 0) ++pieces[(size_t)(x / range)];
-        hp->dec_seg_pieces = std::max<int>(hp->dec_seg_pieces, (int)((x + nst - 1) / range - x / range + 1));
+        hp->dec_seg_pieces = std::max<int>(hp->dec_seg_pieces, (int)((x + nwork - 1) / range - x / range + 1));
       }
       }
     }
@@ -1838,7 +1862,7 @@ void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
         a->tabs.dec_r0[e] = r0 + i * T;
         a->tabs.dec_ctx[e] = prefix + t1;
         a->tabs.dec_ntok[e] = t1 - i * T;
-        unit += hkv * dec_stages(prefix + t1);
+        unit += hkv * dec_units_of(prefix + t1, a->dec_piece);
       }
     }
   }
@@ -1972,6 +1996,7 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   a.n_chunk_items = hp.n_chunk_items;
   a.ch_target = hp.ch_target;
   a.dec_units = hp.dec_units;
+  a.dec_piece = hp.dec_piece;
   a.dec_range = hp.dec_range;
   a.dec_pmax = hp.dec_pmax;
   a.num_pages = layout->num_pages;

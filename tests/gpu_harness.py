@@ -20,12 +20,12 @@ def layout_of(case):
                            lay["page_size"], lay["num_pages"], lay["k_format"], lay["v_format"])
 
 
-def batch_of(q_start, prefix_len, block_table, device="cuda"):
+def batch_of(q_start, prefix_len, block_table, device="cuda", flags=0):
     qs = np.ascontiguousarray(q_start, dtype=np.int32)
     pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     return mab.BatchDesc(torch.from_numpy(qs).to(device), torch.from_numpy(pl).to(device),
-                         torch.from_numpy(bt).to(device), qs, pl)
+                         torch.from_numpy(bt).to(device), qs, pl, flags=flags)
 
 
 class GpuState:

@@ -64,7 +64,8 @@ static int run(uint64_t seed, bool may_launch) {
   B.num_rows = q_start[num_seqs] + (uni(0, 100) == 0 ? 1 : 0);  // sometimes inconsistent
   const int64_t ps = L.page_size > 0 ? L.page_size : 16;
   B.max_pages_per_seq = (int32_t)std::min<int64_t>(1 << 30, (max_ctx + ps - 1) / ps + (uni(0, 50) == 0 ? -1 : 0));
-  B.reserved = 0;
+  B.flags = uni(0, 1) ? MAB_BATCH_INVARIANT : 0;
+  if (uni(0, 100) == 0) B.flags = (int32_t)uni(2, 9);  // unknown flag bits: refused
   B.q_start = (const int32_t*)kFakeDev;
   B.prefix_len = (const int32_t*)kFakeDev;
   B.block_table = (const int32_t*)kFakeDev;

@@ -51,11 +51,11 @@ def test_status_strings():
 
 
 class _HostBatch:
-    def __init__(self, q_start, prefix_len, max_pages=64, dev_ptrs=True):
+    def __init__(self, q_start, prefix_len, max_pages=64, dev_ptrs=True, flags=0):
         self.qs = np.ascontiguousarray(q_start, np.int32)
         self.pl = np.ascontiguousarray(prefix_len, np.int32)
         ptr = FAKE_DEV if dev_ptrs else 0
-        self.struct = mab.Batch(len(self.pl), int(self.qs[-1]), max_pages, 0, ptr, ptr, ptr,
+        self.struct = mab.Batch(len(self.pl), int(self.qs[-1]), max_pages, flags, ptr, ptr, ptr,
                                 self.qs.ctypes.data, self.pl.ctypes.data)
 
 
@@ -143,6 +143,28 @@ def test_workspace_large_batch_holds_tables():
     small = _HostBatch(list(range(97)), [100] * 96, max_pages=16)
     big = _HostBatch(list(range(98)), [100] * 97, max_pages=16)
     assert _ws(lay, big) - _ws(lay, small) >= 4 * (4 * 97 + 1 + 1)
+
+
+def test_workspace_closed_form_batch_invariant():
+    """With MAB_BATCH_INVARIANT every decode segment (row x KV head) is cut
+    into pieces of 512 keys (16 stages) from its own first key, one piece per
+    worker: a partial slot per piece, whatever else is in the batch."""
+    lay = mab.make_layout(24, 4, 128, 256, 1000)
+    ctxs = [1, 511, 512, 513, 5000, 40000]
+    b = _HostBatch(list(range(len(ctxs) + 1)), [c - 1 for c in ctxs], max_pages=200,
+                   flags=mab.MAB_BATCH_INVARIANT)
+    pieces = sum(4 * -(-(-(-c // 32)) // 16) for c in ctxs)
+    align = lambda x: -(-x // 256) * 256
+    assert _ws(lay, b) == align(pieces * 6 * 128 * 4) + align(pieces * 6 * 8) + align(len(ctxs) * 4 * 16)
+    # the same rows in another batch take the same pieces: the slots add up
+    b1 = _HostBatch([0, 1], [ctxs[-1] - 1], max_pages=200, flags=mab.MAB_BATCH_INVARIANT)
+    assert _ws(lay, b1) == align(4 * 79 * 6 * 128 * 4) + align(4 * 79 * 6 * 8) + align(4 * 16)
+
+
+@pytest.mark.parametrize("flags", [2, 3, 1 << 30, -1])
+def test_unknown_batch_flags_are_refused(flags):
+    lay = mab.make_layout(24, 4, 128, 256, 100)
+    assert _ws(lay, _HostBatch([0, 1], [5], flags=flags)) == -2
 
 
 @pytest.mark.parametrize("mutate,status", [
