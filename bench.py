@@ -159,8 +159,10 @@ def chunk_flops(case):
     return f
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The oracle on whole sequences of the case, in order, until the budget is spent."""
+def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
+    """The oracle on whole sequences of the case, shortest first, until the
+    budget is spent; a sequence whose predicted time (from the rate so far per
+    row-key pair and per key) would take the total past cap_s is not started."""
     import torch
     from threadpoolctl import threadpool_info
 
@@ -172,9 +174,13 @@ def cpu_baseline(case, budget_s=12.0):
     kp = ocache.new_pool(lay, lay["k_format"])
     vp = ocache.new_pool(lay, lay["v_format"])
     order = sorted(range(case.num_seqs), key=lambda s: case.context(s))  # short first
-    done, nbytes, rows, elapsed = [], 0, 0, 0.0
+    done, nbytes, rows, elapsed, work = [], 0, 0, 0.0, 0.0
     for s in order:
         r0, r1 = int(case.q_start[s]), int(case.q_start[s + 1])
+        w = (r1 - r0 + 1) * float(case.context(s))  # attention pairs plus the keys encoded
+        if done and elapsed + elapsed / work * w > cap_s:
+            break
+        work += w
         k = torch.cat([case.k_prefix[s].cpu(), case.k_new[r0:r1].cpu()]).numpy()
         v = torch.cat([case.v_prefix[s].cpu(), case.v_new[r0:r1].cpu()]).numpy()
         q = case.q.cpu().numpy()
