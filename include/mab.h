@@ -115,8 +115,10 @@ typedef struct mab_kv_layout {
  * MAB_INVARIANT_PIECE_KEYS from its own first key and each piece runs on its
  * own wave.  Prefill-chunk rows are batch-independent either way: their key
  * splits depend only on their own tile count and the device's compute-unit
- * count.  Cost on one MI355X: about +30% on a batch of 16 short decode rows,
- * +15% on 4-token verify rows, nothing on single long rows. */
+ * count.  The grouping of a verify row's tokens depends only on its own
+ * length and the layout.  Cost on one MI355X: about +30% on a batch of 16
+ * short decode rows, +15% on 4-token verify rows, nothing on single long
+ * rows. */
 enum { MAB_BATCH_INVARIANT = 1 };
 #define MAB_INVARIANT_PIECE_KEYS 512
 
@@ -180,10 +182,11 @@ int32_t kv_append_quant(const mab_kv_layout* layout, const mab_batch* batch,
  * is deterministic (bit-identical run to run) and independent of the
  * physical page ids.  Sequences of more than 16 rows (prefill chunks) get
  * results that are also bit-identical whatever else shares the batch.  Shorter
- * sequences (decode rows, and verify rows of 2-16 tokens, which run in groups
- * of 16/(Hq/Hkv) rows on the decode path) have their key ranges cut according
- * to the whole batch, so they may differ in the last bits (within 1e-3 at
- * unit-scale values) between different batches.
+ * sequences (decode rows, and verify rows of 2-16 tokens, which run on the
+ * decode path in groups of 16/G rows, G = Hq/Hkv, or of 32/G rows over
+ * quantized pools when the sequence has more than 16/G rows) have their key
+ * ranges cut according to the whole batch, so they may differ in the last
+ * bits (within 1e-3 at unit-scale values) between different batches.
  *
  * q          : device fp16 [num_rows][Hq][D], read only.
  * k_pool, v_pool : device pools, read only.

@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "mab.h"
@@ -46,6 +47,18 @@ __device__ inline u32x4_t gload16_nt(const void* p) {
   return __builtin_nontemporal_load((const MAB_GLOBAL u32x4_t*)p);
 }
 __device__ inline int32_t gload_i32(const int32_t* p) { return *(const MAB_GLOBAL int32_t*)p; }
+// Raw buffer resources: a wave-uniform base and a size in bytes; a load at an
+// offset at or past the size returns zeros and touches no memory.  Word 3 is
+// the gfx9 descriptor word for untyped 32-bit accesses.
+constexpr int kCpolNt = 2;  // cache policy: non-temporal (streamed once)
+__device__ inline __amdgpu_buffer_rsrc_t run_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Debug mode (MAB_DEBUG=1 in the environment of the calling process): every
 // page id read from the block table is checked against the pool; an id
@@ -114,14 +127,19 @@ __host__ __device__ inline int chunk_heads(int group) { return group % 4 == 0 ? 
 __host__ __device__ inline int chunk_rows(int group) { return 32 * kMixedWaves / chunk_heads(group); }
 
 // Rows of a sequence with q_len <= kMaxVerify (decode rows and short verify
-// rows) run on the decode path, in sub-rows of at most dec_tokens(G)
-// consecutive rows whose (row, head) pairs fill the 16 MFMA slots of a decode
-// wave; sub-row i holds rows [i*T, min(q_len, (i+1)*T)) and streams the keys
-// its last row sees.  Longer sequences are prefill chunks.
+// rows) run on the decode path, in sub-rows of at most T consecutive rows
+// whose (row, head) pairs fill the MFMA slots of a decode wave: one group of
+// 16 slots (T = 16/G), or, for a sequence with more than 16/G rows over
+// quantized pools (`wide`), two groups of 16 that share every stage read
+// (T = 32/G).  Sub-row i holds rows [i*T, min(q_len, (i+1)*T)) and streams
+// the keys its last row sees.  Longer sequences are prefill chunks.
 __host__ __device__ inline bool is_chunk(int q_len) { return q_len > kMaxVerify; }
-__host__ __device__ inline int dec_tokens(int group) { return 16 / group; }
-__host__ __device__ inline int dec_subrows(int q_len, int group) {
-  return (q_len + dec_tokens(group) - 1) / dec_tokens(group);
+__host__ __device__ inline int dec_tokens(int q_len, int group, bool wide) {
+  return wide && q_len > 16 / group ? 32 / group : 16 / group;
+}
+__host__ __device__ inline int dec_subrows(int q_len, int group, bool wide) {
+  const int t = dec_tokens(q_len, group, wide);
+  return (q_len + t - 1) / t;
 }
 
 // A prefill chunk: ceil(q_len/rows) row tiles x Hkv x G/H head groups, each
@@ -308,6 +326,7 @@ struct Group {
   float4_t o[2 * NB];     // O^T tile t of block t/2: slot l%16, rows 4(l/16) + [0,4), row r being value
                           // 2r + t%2 of the block; V codes taken with their bias
   float4_t vb[NB];        // per block: sum over keys of the P * V-scale weights (the bias correction of o)
+  float vs[NB];           // the same sums, lane-partial (two-group waves: the MFMA form costs 12 more registers)
   float m, l;             // running max (log2 units) and lane-partial sum
   int limit;              // last key position visible to the slot (-1: none)
 };
@@ -371,10 +390,30 @@ struct DecLayout {
   static constexpr int kLoads = (kChunks + 63) / 64;          // 16-byte loads per lane per stage
   static constexpr int kKOff = 0;
   static constexpr int kVOff = kKBytes;
-  static constexpr int kRawBytes = kLoads * 1024 + 16;        // tail lanes + over-read pad
+  static constexpr int kRawBytes = kLoads * 1024 + 16;        // one stage buffer: tail lanes + over-read pad
   static constexpr int kSKOff = kRawBytes;                    // float [NB][32]: K scale * c
   static constexpr int kSVOff = kSKOff + NB * kStepKeys * 4;  // half  [NB][32]: V scale
   static constexpr int kWaveBytes = kSVOff + NB * kStepKeys * 2;
+  // kernels with wide verify pieces (quantized pools): a second stage buffer
+  // after the scales, for the two-buffer ring of those pieces
+  static constexpr bool kWideOk = KF != MAB_KV_F16 && VF != MAB_KV_F16;
+  static constexpr int kWideBytes = kWaveBytes + kRawBytes;
+  // The stage as four 16-key runs of 16-byte chunks, each contiguous in its
+  // pool: K of keys 0-15, K of keys 16-31, V of keys 0-15, V of keys 16-31
+  // (a run of 16 keys holds kRecK, resp. kRecV, chunks).  Run q covers
+  // chunks [run_lo(q), run_lo(q+1)); the last run also takes the lanes past
+  // the last chunk (they read zeros).  run_load_issues: the loads of a stage
+  // loaded run by run (one per run that meets each 64-chunk load).
+  static constexpr int run_lo(int q) {
+    return q == 0 ? 0 : q == 1 ? kRecK : q == 2 ? 2 * kRecK : q == 3 ? 2 * kRecK + kRecV : 64 * kLoads;
+  }
+  static constexpr bool run_meets(int q, int i) { return run_lo(q) < 64 * i + 64 && run_lo(q + 1) > 64 * i; }
+  static constexpr int run_load_issues() {
+    int n = 0;
+    for (int i = 0; i < kLoads; ++i)
+      for (int q = 0; q < 4; ++q) n += run_meets(q, i) ? 1 : 0;
+    return n;
+  }
   static_assert(kKBytes % 16 == 0 && kVBytes % 16 == 0 && kWaveBytes % 16 == 0, "alignment");
 };
 
@@ -535,14 +574,68 @@ struct DecWave {
   }
 };
 
-// Pulls the K and V block scales of the stage in LDS into the compact arrays:
+// One buffer load of a stage loaded run by run: load I (chunks 64I..64I+63)
+// for the lanes whose chunk lies in run Q.  The byte of the run at lane 0 of
+// the load goes in the instruction's offset field when it is not negative
+// (a run that starts inside the load: into the lane offset; the lanes before
+// the run start are off).  The offset field moves the LDS address as well as
+// the memory address, so the LDS base given is that much lower.
+template <int NB, int KF, int VF, int I, int Q>
+__device__ __attribute__((always_inline)) inline void dec_run_load(const __amdgpu_buffer_rsrc_t (&r)[4], uint32_t voff,
+                                                                   uint8_t* buf, int lane) {
+  using L = DecLayout<NB, KF, VF>;
+  if constexpr (L::run_meets(Q, I)) {
+    constexpr int shift = 1024 * I - 16 * L::run_lo(Q);
+    static_assert(shift < 4096, "the offset field holds 12 bits");
+    constexpr bool whole = L::run_lo(Q) <= 64 * I && L::run_lo(Q + 1) >= 64 * I + 64;
+    const int ch = lane + 64 * I;
+    using lds_t = __attribute__((address_space(3))) void*;
+    if (whole || (ch >= L::run_lo(Q) && ch < L::run_lo(Q + 1))) {
+      if constexpr (shift >= 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r[Q], (lds_t)(buf + 1024 * I - shift), 16, voff, 0, shift, kCpolNt);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r[Q], (lds_t)(buf + 1024 * I), 16, voff + shift, 0, 0, kCpolNt);
+    }
+  }
+}
+
+template <int NB, int KF, int VF, int... IQ>
+__device__ __attribute__((always_inline)) inline void dec_run_loads(const __amdgpu_buffer_rsrc_t (&r)[4], uint32_t voff,
+                                                                    uint8_t* buf, int lane,
+                                                                    std::integer_sequence<int, IQ...>) {
+  (dec_run_load<NB, KF, VF, IQ / 4, IQ % 4>(r, voff, buf, lane), ...);
+}
+
+// Loads the 32 keys of a stage straight into the LDS stage buffer buf, run
+// by run (run bases k0, k1, v0, v1; run1 false: keys 16-31 are past the
+// piece and read as zeros): chunk c lands at buf + 16c, as the register form
+// stores it.  Issues L::run_load_issues() buffer loads; a load that meets two
+// runs is issued once per run, each for its own lanes.  Each run's resource
+// ends where the run ends, so lanes past it (the tail, or a run that is off)
+// read zeros.
+template <int NB, int KF, int VF>
+__device__ __attribute__((always_inline)) inline void dec_stage_to_lds(uint8_t* buf, const uint8_t* k0,
+                                                                       const uint8_t* k1, const uint8_t* v0,
+                                                                       const uint8_t* v1, bool run1, int lane) {
+  using L = DecLayout<NB, KF, VF>;
+  // the bases and sizes are wave-uniform: say so, so that the resources live
+  // in scalar registers
+  const int on1 = __builtin_amdgcn_readfirstlane(run1 ? 1 : 0);
+  const __amdgpu_buffer_rsrc_t r[4] = {
+      run_rsrc(wave_uniform(k0), 16 * L::kRecK), run_rsrc(wave_uniform(k1), on1 * 16 * L::kRecK),
+      run_rsrc(wave_uniform(v0), 16 * L::kRecV), run_rsrc(wave_uniform(v1), on1 * 16 * L::kRecV)};
+  dec_run_loads<NB, KF, VF>(r, 16u * (uint32_t)lane, buf, lane, std::make_integer_sequence<int, 4 * L::kLoads>{});
+}
+
+// Pulls the K and V block scales of the stage in LDS (stage buffer raw) into
+// the compact arrays of the wave area w:
 // K scales as fp32 times c = sm_scale*log2(e), V scales as fp16, both [block][key].
 // Keys at or past kend get scale 0, so their (possibly NaN) bytes never reach
 // a sum: their logits become exactly 0 before masking and their P*scale 0.
 // Returns (wave-uniform) whether some V scale of the stage is at or above
 // kBigVScaleBits.
 template <int NB, int KF, int VF>
-__device__ inline bool dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
+__device__ inline bool dec_scales(const uint8_t* raw, uint8_t* w, int lane, float zc, int nvalid) {
   using L = DecLayout<NB, KF, VF>;
   bool big = false;
 #pragma unroll
@@ -555,13 +648,13 @@ __device__ inline bool dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
     if (!isv) {
       float d = 1.f;  // the unquantized format has no scale
       if constexpr (KF != MAB_KV_F16)
-        d = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(w + L::kKOff + key * L::kRecK +
+        d = (float)__builtin_bit_cast(half_t, *reinterpret_cast<const uint16_t*>(raw + L::kKOff + key * L::kRecK +
                                                                                   b * L::kBK));
       reinterpret_cast<float*>(w + L::kSKOff)[m] = ok ? d * zc : 0.f;
     } else {
       uint16_t bits = 0x3C00u;  // fp16 1.0
       if constexpr (VF != MAB_KV_F16)
-        bits = *reinterpret_cast<const uint16_t*>(w + L::kVOff + key * L::kRecV + b * L::kBV);
+        bits = *reinterpret_cast<const uint16_t*>(raw + L::kVOff + key * L::kRecV + b * L::kBV);
       reinterpret_cast<uint16_t*>(w + L::kSVOff)[m] = ok ? bits : (uint16_t)0;
       big |= ok && bits >= kBigVScaleBits;  // scales are non-negative: bit order is value order
     }
@@ -569,91 +662,118 @@ __device__ inline bool dec_scales(uint8_t* w, int lane, float zc, int nvalid) {
   return __any(big);
 }
 
-// One 32-key stage of a decode wave: S^T = K Q^T on integer codes per block,
-// fp32 block scales, online softmax with a stale max (rescaled only when the
-// running max grows by more than 2^kRescaleSlack; by any amount in a stage
-// with a large V scale, `big_v`), then O^T += V^T (P * V scale) with P
-// rounded to fp16 once and multiplied by the fp16 V scale of each block.  The
-// normaliser sums the same fp16 P.  The V codes enter with the bias of their
-// conversion; the sum of each block's weights (an MFMA against ones) removes
-// it at the end.  `tail`: the stage holds keys at or past kend, or past the
-// limit of some slot (masked per slot).
-template <int NB, int KF, int VF>
-__device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, int kend, bool tail, bool big_v,
-                                   int lane) {
-  // keys visible to this lane's slot in the stage: below kend and at most gr.limit
+// One 32-key stage of a decode wave over NG slot groups (NG = 2: a wide
+// verify sub-row; both groups share the stage's K and V operands): S^T = K Q^T
+// on integer codes per block, fp32 block scales, online softmax with a stale
+// max (rescaled only when the running max grows by more than 2^kRescaleSlack;
+// by any amount in a stage with a large V scale, `big_v`), then O^T += V^T
+// (P * V scale) with P rounded to fp16 once and multiplied by the fp16 V scale
+// of each block.  The normaliser sums the same fp16 P.  The V codes enter with
+// the bias of their conversion; the sum of each block's weights (an MFMA
+// against ones) removes it at the end.  `raw`: the stage's bytes; `w`: the
+// wave area holding the compact scales.  `tail`: the stage holds keys at or
+// past kend, or past the limit of some slot (masked per slot).
+template <int NB, int KF, int VF, int NG>
+__device__ inline void dec_compute(Group<NB> (&gr)[NG], const uint8_t* raw, const uint8_t* w, int kbase, int kend,
+                                   bool tail, bool big_v, int lane) {
   using L = DecLayout<NB, KF, VF>;
   const int j = lane >> 4, n = lane & 15;
-  float4_t s[2];
+  float4_t s[NG][2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NG; ++k) s[k][kt] = float4_t{0.f, 0.f, 0.f, 0.f};
     const int rec = (16 * kt + n) * L::kRecK;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       half8_t kc;
-      if constexpr (KF == MAB_KV_F16) kc = *reinterpret_cast<const half8_t*>(w + L::kKOff + rec + b * L::kBK + 16 * j);
-      else if constexpr (KF == MAB_KV_Q8) kc = lds_codes8_q8(w + L::kKOff, rec + b * L::kBK + 2 + 8 * j);
-      else kc = lds_codes8_q4(w + L::kKOff, rec + b * L::kBK + 2 + 4 * j);
-      const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, gr.q[b], float4_t{0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0);
+      if constexpr (KF == MAB_KV_F16) kc = *reinterpret_cast<const half8_t*>(raw + L::kKOff + rec + b * L::kBK + 16 * j);
+      else if constexpr (KF == MAB_KV_Q8) kc = lds_codes8_q8(raw + L::kKOff, rec + b * L::kBK + 2 + 8 * j);
+      else kc = lds_codes8_q4(raw + L::kKOff, rec + b * L::kBK + 2 + 4 * j);
       const float4_t kd = *reinterpret_cast<const float4_t*>(w + L::kSKOff + 4 * (b * kStepKeys + 16 * kt + 4 * j));
-      s[kt] += kd * pb;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const float4_t pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, gr[k].q[b], float4_t{0.f, 0.f, 0.f, 0.f},
+                                                                   0, 0, 0);
+        s[k][kt] += kd * pb;
+      }
     }
   }
-  if (tail) {
+  half8_t ph[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    Group<NB>& g = gr[k];
+    if (tail) {
+      // keys visible to this lane's slot in the stage: below kend and at most g.limit
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kbase + 16 * kt + 4 * j + i >= min(kend, g.limit + 1)) s[k][kt][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
+                     fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3])));
+    mx = max_xor32(max_xor16(mx));
+    const bool grow = mx > g.m + (big_v ? 0.f : kRescaleSlack);  // also true for the first keys (m = -inf)
+    if (__any(grow)) {
+      const float m_new = grow ? mx : g.m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(g.m - m_new) : 1.f;  // 0 when m was -inf
+#pragma unroll
+      for (int t = 0; t < 2 * NB; ++t) g.o[t] *= alpha;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (NG == 1) g.vb[b] *= alpha;
+        else g.vs[b] *= alpha;
+      }
+      g.l *= alpha;
+      g.m = m_new;
+    }
+    float p[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (kbase + 16 * kt + 4 * j + i >= min(kend, gr.limit + 1)) s[kt][i] = -INFINITY;
+        p[4 * kt + i] = __builtin_amdgcn_exp2f(s[k][kt][i] - g.m);  // <= 2^kRescaleSlack (1 if big_v); masked 0
+    // P as fp16 in the key order of the PV operand: 4j+[0,4) then 16+4j+[0,4)
+    ph[k] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
+                    (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
+    // the normaliser sums the fp16 weights that the PV products use
+    const half2_t one2 = half2_t{(half_t)1.f, (half_t)1.f};
+    float psum = __builtin_amdgcn_fdot2(half2_t{ph[k][0], ph[k][1]}, one2, 0.f, false);
+    psum = __builtin_amdgcn_fdot2(half2_t{ph[k][2], ph[k][3]}, one2, psum, false);
+    psum = __builtin_amdgcn_fdot2(half2_t{ph[k][4], ph[k][5]}, one2, psum, false);
+    psum = __builtin_amdgcn_fdot2(half2_t{ph[k][6], ph[k][7]}, one2, psum, false);
+    g.l += psum;
   }
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = max_xor32(max_xor16(mx));
-  const bool grow = mx > gr.m + (big_v ? 0.f : kRescaleSlack);  // also true for the first keys (m = -inf)
-  if (__any(grow)) {
-    const float m_new = grow ? mx : gr.m;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(gr.m - m_new) : 1.f;  // 0 when m was -inf
-#pragma unroll
-    for (int t = 0; t < 2 * NB; ++t) gr.o[t] *= alpha;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) gr.vb[b] *= alpha;
-    gr.l *= alpha;
-    gr.m = m_new;
-  }
-  float p[8];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      p[4 * kt + i] = __builtin_amdgcn_exp2f(s[kt][i] - gr.m);  // <= 2^kRescaleSlack (1 if big_v); masked 0
-  // P as fp16 in the key order of the PV operand: 4j+[0,4) then 16+4j+[0,4)
-  const half8_t ph = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
-                             (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
-  // the normaliser sums the fp16 weights that the PV products use
-  const half2_t one2 = half2_t{(half_t)1.f, (half_t)1.f};
-  float psum = __builtin_amdgcn_fdot2(half2_t{ph[0], ph[1]}, one2, 0.f, false);
-  psum = __builtin_amdgcn_fdot2(half2_t{ph[2], ph[3]}, one2, psum, false);
-  psum = __builtin_amdgcn_fdot2(half2_t{ph[4], ph[5]}, one2, psum, false);
-  psum = __builtin_amdgcn_fdot2(half2_t{ph[6], ph[7]}, one2, psum, false);
-  gr.l += psum;
   const half_t* sv = reinterpret_cast<const half_t*>(w + L::kSVOff);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const half4_t s0 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 4 * j);
     const half4_t s1 = *reinterpret_cast<const half4_t*>(sv + b * kStepKeys + 16 + 4 * j);
-    const half8_t pf = ph * half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if constexpr (VBias<VF>::kBias != 0.f) {
-      const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-      gr.vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, gr.vb[b], 0, 0, 0);  // sum of the weights
+    const half8_t svb = half8_t{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    half8_t pf[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      pf[k] = ph[k] * svb;
+      if constexpr (VBias<VF>::kBias != 0.f) {  // sum of the weights
+        if constexpr (NG == 1) {
+          const half8_t ones = half8_t{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+          gr[k].vb[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[k], gr[k].vb[b], 0, 0, 0);
+        } else {
+          const half2_t one2 = half2_t{(half_t)1.f, (half_t)1.f};
+          float t = gr[k].vs[b];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_fdot2(half2_t{pf[k][2 * e], pf[k][2 * e + 1]}, one2, t, false);
+          gr[k].vs[b] = t;
+        }
+      }
     }
     // the block's two V^T tiles: row n of tile t2 is value 2n + t2 of the block
     half2_t vp[2][4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ka = (e < 2) ? 4 * j + 2 * e : 16 + 4 * j + 2 * (e - 2);
-      lds_value_pairs_biased<VF>(w + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
+      lds_value_pairs_biased<VF>(raw + L::kVOff, ka * L::kRecV + b * L::kBV + kPayload<VF>,
                                  (ka + 1) * L::kRecV + b * L::kBV + kPayload<VF>, n, vp[0][e], vp[1][e]);
       if constexpr (VF == MAB_KV_F16) {
         // f16 values of keys past the range are whatever the pool holds there
@@ -671,7 +791,9 @@ __device__ inline void dec_compute(Group<NB>& gr, const uint8_t* w, int kbase, i
     for (int t2 = 0; t2 < 2; ++t2) {
       const half8_t vc = half8_t{vp[t2][0][0], vp[t2][0][1], vp[t2][1][0], vp[t2][1][1],
                                  vp[t2][2][0], vp[t2][2][1], vp[t2][3][0], vp[t2][3][1]};
-      gr.o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf, gr.o[2 * b + t2], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NG; ++k)
+        gr[k].o[2 * b + t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vc, pf[k], gr[k].o[2 * b + t2], 0, 0, 0);
     }
   }
 }
@@ -1037,6 +1159,7 @@ struct AttnArgs {
   int ch_target;            // work-group slots the chunk splits aim to fill
   int dec_units;            // units in the decode stream (stages, plus padding with dec_piece)
   int dec_piece;            // 0: equal ranges over the stream; else stages per piece (MAB_BATCH_INVARIANT)
+  int dec_wide;             // verify sub-rows may take two slot groups (quantized pools)
   int dec_range;            // stages per decode worker (the last may have fewer)
   int dec_pmax;             // partial slots per decode worker
   int dec_slots;            // (row, head) slots of a decode partial: G, or T*G with verify rows
@@ -1124,7 +1247,8 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   const int tn = n / G, hn = n % G;  // this lane's slot: row r0 + tn, head g*G + hn
   const bool live = tn < ntok;
   const int64_t orow = (int64_t)(r0 + tn) * a.hq + g * G + hn;
-  Group<NB> gr;
+  Group<NB> grs[1];
+  Group<NB>& gr = grs[0];
   dec_init<NB, KF>(gr, live ? a.q + orow * D : nullptr, ctx - ntok + tn, lane);
   // a finite floor for the running max: a verify row's slot may see no key of
   // a piece that starts past its limit, and exp2(-inf - floor) is 0, not NaN
@@ -1149,10 +1273,10 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
     const int kbase = kb + st * kStepKeys;
     dw.store(wbuf, lane);
     asm volatile("" ::: "memory");
-    const bool big_v = dec_scales<NB, KF, VF>(wbuf, lane, a.c, ke - kbase);
+    const bool big_v = dec_scales<NB, KF, VF>(wbuf, wbuf, lane, a.c, ke - kbase);
     if (st + DEPTH < nst) issue(dw, st + DEPTH);
     asm volatile("" ::: "memory");
-    dec_compute<NB, KF, VF>(gr, wbuf, kbase, ke, kbase + kStepKeys > kvis, big_v, lane);
+    dec_compute<NB, KF, VF, 1>(grs, wbuf, wbuf, kbase, ke, kbase + kStepKeys > kvis, big_v, lane);
     asm volatile("" ::: "memory");
   };
 #pragma unroll
@@ -1188,10 +1312,130 @@ __device__ inline void decode_piece(const AttnArgs& a, uint8_t* wbuf, int s, int
   if (!whole && j == 0) a.ml_part[pi] = make_float2(gr.m, lsum);
 }
 
+// One piece of a wide verify sub-row (ntok rows, ntok*G > 16 slots): as
+// decode_piece, with two groups of 16 slots that share every stage, slot
+// 16k + n of group k being row r0 + (16k+n)/G, head g*G + (16k+n)%G.  The
+// stage bytes go straight from memory into a ring of two LDS stage buffers
+// (the registers hold the two groups' state instead): stage st + 1 is issued
+// into the buffer that held stage st - 1 before the wave waits for stage st,
+// so one stage is always in flight while another is computed on.  The
+// compiler does not order LDS reads after these loads: the waits are
+// explicit, and the LDS reads of a buffer are complete before it is refilled.
+template <int NB, int KF, int VF, bool DBG>
+__device__ inline void decode_piece_wide(const AttnArgs& a, uint8_t* wbuf, int s, int r0, int ntok, int ctx, int g,
+                                         int kb, int ke, bool whole, int64_t slot) {
+  using L = DecLayout<NB, KF, VF>;
+  static_assert(L::kWideOk, "quantized pools only");
+  // every argument is the same across the wave: say so, so that the stage
+  // loop and the page walk run on the scalar unit
+  s = __builtin_amdgcn_readfirstlane(s);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  ntok = __builtin_amdgcn_readfirstlane(ntok);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
+  g = __builtin_amdgcn_readfirstlane(g);
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
+  constexpr int D = 32 * NB;
+  const int lane = threadIdx.x & 63;
+  const int G = a.hq / a.hkv;
+  const int n = lane & 15, j = lane >> 4;
+  const int32_t* bt_row = a.block_table + (int64_t)s * a.max_pages;
+  const int nst = ceil_div(ke - kb, kStepKeys);
+  // page ids of the piece's 16-key runs, 64 at a time (one per lane)
+  auto page_window = [&](int win) {
+    const int key = kb + 16 * (64 * win + lane);
+    return key < ke ? checked_page(gload_i32(bt_row + key / a.page_size), a.num_pages, DBG) : 0;
+  };
+  int my_page = page_window(0);
+  Group<NB> gr[2];
+  bool live[2];
+  int64_t orow[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tn = (16 * k + n) / G, hn = (16 * k + n) % G;
+    live[k] = tn < ntok;
+    orow[k] = (int64_t)(r0 + tn) * a.hq + g * G + hn;
+    dec_init<NB, KF>(gr[k], live[k] ? a.q + orow[k] * D : nullptr, ctx - ntok + tn, lane);
+    gr[k].m = kDecodeMaxFloor;  // finite: a slot may see no key of the piece
+#pragma unroll
+    for (int b = 0; b < NB; ++b) gr[k].vs[b] = 0.f;
+  }
+  const int kvis = min(ke, ctx - ntok + 1);  // keys below this are visible to every live slot
+  auto page_of_run = [&](int run) {
+    if (run > 0 && (run & 63) == 0) {
+      my_page = page_window(run >> 6);
+      // wait here, on the rare path: a wait at the read below would sit on
+      // every stage and hold the next stage's issue back for this one
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    return __builtin_amdgcn_readlane(my_page, run & 63);
+  };
+  // the ring: stage buffer 0 at the start of the wave area, 1 after the scales
+  auto stage_buf = [&](int st) { return (st & 1) ? wbuf + L::kWaveBytes : wbuf; };
+  auto issue = [&](int st) {
+    const int key0 = kb + st * kStepKeys, key1 = key0 + 16;
+    const int p0 = page_of_run(2 * st);
+    const int p1 = __builtin_amdgcn_readlane(my_page, (2 * st + 1) & 63);  // same window: 2*st is even
+    const int64_t tok0 = ((int64_t)p0 * a.hkv + g) * a.page_size + key0 % a.page_size;
+    const int64_t tok1 = ((int64_t)p1 * a.hkv + g) * a.page_size + key1 % a.page_size;
+    dec_stage_to_lds<NB, KF, VF>(stage_buf(st), a.k_pool + tok0 * L::kRecK,
+                                 a.k_pool + tok1 * L::kRecK, a.v_pool + tok0 * L::kRecV, a.v_pool + tok1 * L::kRecV,
+                                 key1 < ke, lane);
+  };
+  issue(0);
+  for (int st = 0; st < nst; ++st) {
+    const int kbase = kb + st * kStepKeys;
+    if (st + 1 < nst) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage st - 1's reads of the buffer are done
+      issue(st + 1);
+      wait_vmcnt<L::run_load_issues()>();  // all but stage st + 1's loads have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    const uint8_t* raw = stage_buf(st);
+    const bool big_v = dec_scales<NB, KF, VF>(raw, wbuf, lane, a.c, ke - kbase);
+    dec_compute<NB, KF, VF, 2>(gr, raw, wbuf, kbase, ke, kbase + kStepKeys > kvis, big_v, lane);
+    asm volatile("" ::: "memory");
+  }
+  float lsum[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    lsum[k] = gr[k].l;
+    lsum[k] += __shfl_xor(lsum[k], 16);
+    lsum[k] += __shfl_xor(lsum[k], 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      gr[k].vs[b] += __shfl_xor(gr[k].vs[b], 16);
+      gr[k].vs[b] += __shfl_xor(gr[k].vs[b], 32);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (!live[k]) continue;
+    if constexpr (VBias<VF>::kBias != 0.f) {  // remove the code bias
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) gr[k].o[2 * b + t2] -= VBias<VF>::kBias * gr[k].vs[b];
+    }
+    const float inv = whole ? 1.f / lsum[k] : 1.f;
+    const int64_t pi = slot * a.dec_slots + 16 * k + n;
+    float* dst = whole ? a.out + orow[k] * D : a.o_part + pi * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float4_t* ob = &gr[k].o[2 * b];
+      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j) = float4_t{ob[0][0], ob[1][0], ob[0][1], ob[1][1]} * inv;
+      *reinterpret_cast<float4_t*>(dst + 32 * b + 8 * j + 4) =
+          float4_t{ob[0][2], ob[1][2], ob[0][3], ob[1][3]} * inv;
+    }
+    if (!whole && j == 0) a.ml_part[pi] = make_float2(gr[k].m, lsum[k]);
+  }
+}
+
 // Decode worker w (one wave): stages [w*R, min((w+1)*R, units)) of the decode
 // stream, one piece per segment it touches.  The worker that runs a segment's
 // first stage records where the segment's results went.
-template <int NB, int KF, int VF, int DEPTH, bool DBG>
+template <int NB, int KF, int VF, int DEPTH, bool DBG, bool WIDE>
 __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
   const int x0 = w * a.dec_range, x1 = min(x0 + a.dec_range, a.dec_units);
   if (x0 >= x1) return;
@@ -1210,8 +1454,13 @@ __device__ inline void decode_worker(const AttnArgs& a, uint8_t* wbuf, int w) {
       const int r0 = tv.dec_r0[e];
       const bool first = x == seg_lo, whole = first && p_hi >= work_hi;
       const int64_t slot = (int64_t)w * a.dec_pmax + k;
-      decode_piece<NB, KF, VF, DEPTH, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, (x - seg_lo) * kStepKeys,
-                                           min(ctx, (p_hi - seg_lo) * kStepKeys), whole, slot);
+      const int kb = (x - seg_lo) * kStepKeys, ke = min(ctx, (p_hi - seg_lo) * kStepKeys);
+      bool wide = false;  // more than 16 slots: two slot groups
+      if constexpr (WIDE) {
+        wide = ntok * G > 16;
+        if (wide) decode_piece_wide<NB, KF, VF, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, kb, ke, whole, slot);
+      }
+      if (!wide) decode_piece<NB, KF, VF, DEPTH, DBG>(a, wbuf, tv.dec_seq[e], r0, ntok, ctx, g, kb, ke, whole, slot);
       if (first && (threadIdx.x & 63) == 0) {
         DirEntry d;
         d.slot = (int)slot;
@@ -1465,7 +1714,7 @@ __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   }
 }
 
-template <int NB, int KF, int VF, bool HAS_CHUNK, bool DBG>
+template <int NB, int KF, int VF, bool HAS_CHUNK, bool DBG, bool WIDE>
 __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
   const int b = blockIdx.x;
   if constexpr (HAS_CHUNK) {
@@ -1476,39 +1725,45 @@ __device__ inline void attention_body(const AttnArgs& a, uint8_t* smem) {
   }
   constexpr int nw = HAS_CHUNK ? kMixedWaves : kDecodeWaves;
   const int wave = threadIdx.x >> 6;
-  decode_worker<NB, KF, VF, kDecodeDepth, DBG>(a, smem + wave * DecLayout<NB, KF, VF>::kWaveBytes,
+  using L = DecLayout<NB, KF, VF>;
+  decode_worker<NB, KF, VF, kDecodeDepth, DBG, WIDE>(a, smem + wave * (WIDE ? L::kWideBytes : L::kWaveBytes),
                                          (b - a.n_chunk_items) * nw + wave);
 }
 
-template <int NB, int KF, int VF>
+// One stage buffer per wave, two with wide verify pieces (WIDE).
+template <int NB, int KF, int VF, bool WIDE>
 constexpr int decode_smem_bytes(int waves) {
-  return waves * DecLayout<NB, KF, VF>::kWaveBytes;  // one stage buffer per wave
+  return waves * (WIDE ? DecLayout<NB, KF, VF>::kWideBytes : DecLayout<NB, KF, VF>::kWaveBytes);
 }
 
-template <int NB, int KF, int VF>
+template <int NB, int KF, int VF, bool WIDE>
 constexpr int mixed_smem_bytes() {
-  const int dec = decode_smem_bytes<NB, KF, VF>(kMixedWaves);
+  const int dec = decode_smem_bytes<NB, KF, VF, WIDE>(kMixedWaves);
   const int chunk = 2 * (int)sizeof(ChunkTile<NB>);
   return dec > chunk ? dec : chunk;
 }
 
+// The decode path comes in two builds: without and with the wide verify
+// pieces.  A batch whose decode rows all fit one slot group takes the first,
+// whose registers and waits the second's code would otherwise disturb.
+
 // Batches with a chunk: chunk tiles and decode stream ranges in one launch of
 // kMixedWaves-wave work-groups, two waves per SIMD (one work-group per
 // compute unit).
-template <int NB, int KF, int VF, bool DBG>
+template <int NB, int KF, int VF, bool DBG, bool WIDE>
 __global__ void __launch_bounds__(64 * kMixedWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 mixed_attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF>()];
-  attention_body<NB, KF, VF, true, DBG>(a, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_smem_bytes<NB, KF, VF, WIDE>()];
+  attention_body<NB, KF, VF, true, DBG, WIDE>(a, smem);
 }
 
 // Decode-only batches: kDecodeWaves waves per work-group, two per SIMD (room
 // for two stages in flight per wave).
-template <int NB, int KF, int VF, bool DBG>
+template <int NB, int KF, int VF, bool DBG, bool WIDE>
 __global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 decode_attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF>(kDecodeWaves)];
-  attention_body<NB, KF, VF, false, DBG>(a, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[decode_smem_bytes<NB, KF, VF, WIDE>(kDecodeWaves)];
+  attention_body<NB, KF, VF, false, DBG, WIDE>(a, smem);
 }
 
 // Merges the pieces of decode segments that span several decode workers.
@@ -1653,7 +1908,7 @@ plan_kernel(AttnArgs a) {
       v[2] += 1;
       v[3] += tiles * chunk_split(tiles, a.ch_target);
     } else {
-      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+      for (int i = 0, T = dec_tokens(q_len, G, a.dec_wide); i < dec_subrows(q_len, G, a.dec_wide); ++i) {
         v[0] += 1;
         v[1] += a.hkv * dec_units_of(ctx - q_len + min(q_len, (i + 1) * T), a.dec_piece);
       }
@@ -1689,7 +1944,7 @@ plan_kernel(AttnArgs a) {
       w[t.ch_split + c] = f;
       base[3] += tiles * f;
     } else {
-      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+      for (int i = 0, T = dec_tokens(q_len, G, a.dec_wide); i < dec_subrows(q_len, G, a.dec_wide); ++i) {
         const int e = base[0]++, t1 = min(q_len, (i + 1) * T);
         w[t.dec_unit + e] = base[1];
         w[t.dec_seq + e] = s;
@@ -1712,6 +1967,19 @@ plan_kernel(AttnArgs a) {
 
 bool fmt_ok(int32_t f) { return f == MAB_KV_Q8 || f == MAB_KV_Q4 || f == MAB_KV_F16; }
 
+// Verify sub-rows take two slot groups over quantized pools (the unquantized
+// format's stage is too large for the two-buffer ring of the wide path) when
+// some decode-path sequence has more than 16/G rows.
+bool dec_wide_of(const mab_kv_layout* L, const mab_batch* B) {
+  if (L->k_format == MAB_KV_F16 || L->v_format == MAB_KV_F16) return false;
+  const int G = L->num_q_heads / L->num_kv_heads;
+  for (int s = 0; s < B->num_seqs; ++s) {
+    const int64_t q_len = (int64_t)B->q_start_host[s + 1] - B->q_start_host[s];
+    if (q_len <= kMaxVerify && q_len > 16 / G) return true;  // a decode-path sequence past one slot group
+  }
+  return false;
+}
+
 int check_layout(const mab_kv_layout* L) {
   if (!L) return MAB_ERR_NULL;
   if (L->num_q_heads < 1 || L->num_kv_heads < 1 || L->num_q_heads % L->num_kv_heads) return MAB_ERR_SHAPE;
@@ -1728,6 +1996,7 @@ struct HostPlan {
   bool ch_splits = false;  // some chunk tile is cut into several splits
   int dec_units = 0, dec_wgs = 0, dec_range = 1, dec_pmax = 1;
   int dec_piece = 0;       // stages per piece with MAB_BATCH_INVARIANT, else 0
+  bool dec_wide = false;   // some decode sub-row takes two slot groups
   int dec_seg_pieces = 1;  // pieces of the most cut decode segment
   int dec_slots = 1;       // (row, head) slots per decode partial
   int64_t n_slots = 0;
@@ -1756,6 +2025,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   if (!B->q_start || !B->prefix_len || !B->block_table || !B->q_start_host || !B->prefix_len_host)
     return MAB_ERR_NULL;
   if (B->q_start_host[0] != 0 || B->q_start_host[B->num_seqs] != B->num_rows) return MAB_ERR_SHAPE;
+  const bool wide = dec_wide_of(L, B);
   const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
   const int cus = device_cus();
   const int ch_target = cus;  // resident chunk work-groups: one per compute unit
@@ -1774,7 +2044,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
       items += (int64_t)tiles * f;
       ch_splits |= f > 1;
     } else {
-      const int T = dec_tokens(G), nsub = dec_subrows((int)q_len, G);
+      const int T = dec_tokens((int)q_len, G, wide), nsub = dec_subrows((int)q_len, G, wide);
       for (int i = 0; i < nsub; ++i)
         units += (int64_t)hkv * dec_units_of((int)(prefix + std::min<int64_t>(q_len, (int64_t)(i + 1) * T)), piece);
       n_dec += nsub;
@@ -1790,6 +2060,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
   hp->ch_splits = ch_splits;
   hp->dec_units = (int)units;
   hp->dec_piece = piece;
+  hp->dec_wide = wide;
   hp->dec_slots = max_ntok * G;
   if (units > 0) {
     // equal ranges, one per decode worker (a wave), as many as the device
@@ -1813,7 +2084,7 @@ int check_batch(const mab_kv_layout* L, const mab_batch* B, HostPlan* hp) {
     for (int s = 0; s < B->num_seqs; ++s) {
       const int q_len = B->q_start_host[s + 1] - B->q_start_host[s];
       if (is_chunk(q_len)) continue;
-      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i) {
+      for (int i = 0, T = dec_tokens(q_len, G, wide); i < dec_subrows(q_len, G, wide); ++i) {
       const int ctx = B->prefix_len_host[s] + std::min(q_len, (i + 1) * T);
       const int nst = dec_units_of(ctx, piece), nwork = dec_stages(ctx);
       for (int g = 0; g < hkv; ++g, x += nst) {
@@ -1841,6 +2112,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // The launch-order tables in the kernel arguments (small batches).
 void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
   const int G = L->num_q_heads / L->num_kv_heads, hkv = L->num_kv_heads;
+  const bool wide = a->dec_wide != 0;
   int e = 0, c = 0, unit = 0, item = 0;
   for (int s = 0; s < B->num_seqs; ++s) {
     const int r0 = B->q_start_host[s], q_len = B->q_start_host[s + 1] - r0, prefix = B->prefix_len_host[s];
@@ -1855,7 +2127,7 @@ void fill_arg_tabs(const mab_kv_layout* L, const mab_batch* B, AttnArgs* a) {
       item += tiles * f;
       ++c;
     } else {
-      for (int i = 0, T = dec_tokens(G); i < dec_subrows(q_len, G); ++i, ++e) {
+      for (int i = 0, T = dec_tokens(q_len, G, wide); i < dec_subrows(q_len, G, wide); ++i, ++e) {
         const int t1 = std::min(q_len, (i + 1) * T);
         a->tabs.dec_unit[e] = unit;
         a->tabs.dec_seq[e] = s;
@@ -1881,12 +2153,25 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
                      B->max_pages_per_seq, L->num_kv_heads, L->head_dim, L->page_size, L->num_pages);
 }
 
+template <int NB, int KF, int VF, bool DBG, bool WIDE>
+void launch_attention_build(const AttnArgs& a, int grid, hipStream_t st) {
+  if (a.n_chunk_items > 0)
+    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kMixedWaves), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kDecodeWaves), 0, st,
+                       a);
+}
+
 template <int NB, int KF, int VF, bool DBG>
 void launch_attention_dbg(const AttnArgs& a, int grid, hipStream_t st) {
-  if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF, DBG>), dim3(grid), dim3(64 * kMixedWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF, DBG>), dim3(grid), dim3(64 * kDecodeWaves), 0, st, a);
+  if constexpr (DecLayout<NB, KF, VF>::kWideOk) {
+    if (a.dec_wide) {
+      launch_attention_build<NB, KF, VF, DBG, true>(a, grid, st);
+      return;
+    }
+  }
+  launch_attention_build<NB, KF, VF, DBG, false>(a, grid, st);
 }
 
 // Debug mode takes instantiations of their own: the page-id checks stay out
@@ -1997,6 +2282,7 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   a.ch_target = hp.ch_target;
   a.dec_units = hp.dec_units;
   a.dec_piece = hp.dec_piece;
+  a.dec_wide = hp.dec_wide ? 1 : 0;
   a.dec_range = hp.dec_range;
   a.dec_pmax = hp.dec_pmax;
   a.num_pages = layout->num_pages;
@@ -2022,12 +2308,12 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   }
   if (hp.n_dec > 0) {
     const int nwg = hp.n_dec * layout->num_kv_heads * hp.dec_slots;
-    const bool wide = hp.dec_seg_pieces > kCombineWidePieces;
+    const bool many = hp.dec_seg_pieces > kCombineWidePieces;
     if (layout->head_dim == 64) {
-      if (wide) hipLaunchKernelGGL((combine_kernel<32, 2, 2>), dim3(nwg * 2), dim3(32 * 8), 0, hs, a);
+      if (many) hipLaunchKernelGGL((combine_kernel<32, 2, 2>), dim3(nwg * 2), dim3(32 * 8), 0, hs, a);
       else hipLaunchKernelGGL((combine_kernel<8, 2, 1>), dim3(nwg), dim3(8 * 16), 0, hs, a);
     } else {
-      if (wide) hipLaunchKernelGGL((combine_kernel<32, 4, 4>), dim3(nwg * 4), dim3(32 * 8), 0, hs, a);
+      if (many) hipLaunchKernelGGL((combine_kernel<32, 4, 4>), dim3(nwg * 4), dim3(32 * 8), 0, hs, a);
       else hipLaunchKernelGGL((combine_kernel<8, 4, 1>), dim3(nwg), dim3(8 * 32), 0, hs, a);
     }
   }

@@ -117,22 +117,27 @@ def test_workspace_closed_form():
     assert n == o + ml + cho + chml + dirs
 
 
-def test_workspace_closed_form_verify_rows():
-    # a 5-row verify sequence at G = 6 runs as decode sub-rows of 16 // 6 = 2
-    # rows (2, 2, 1: contexts prefix + 2, + 4, + 5), so a partial holds
-    # 2 * 6 = 12 (row, head) slots; 17 rows are the shortest prefill chunk
-    lay = mab.make_layout(24, 4, 128, 256, 1000)
+@pytest.mark.parametrize("fmt", ["f16", "q8"])
+def test_workspace_closed_form_verify_rows(fmt):
+    # A 5-row verify sequence at G = 6.  Over f16 pools it runs as decode
+    # sub-rows of 16 // 6 = 2 rows (2, 2, 1: contexts prefix + 2, + 4, + 5),
+    # so a partial holds 2 * 6 = 12 (row, head) slots.  Over quantized pools a
+    # sequence with more than 16 // 6 rows takes two slot groups per wave:
+    # sub-rows of 32 // 6 = 5 rows, one sub-row (context prefix + 5) and
+    # 5 * 6 = 30 slots.  17 rows are the shortest prefill chunk.
+    lay = mab.make_layout(24, 4, 128, 256, 1000, fmt, fmt)
     b = _HostBatch([0, 5, 6, 23], [300, 1000, 50], max_pages=400)
     n = _ws(lay, b)
-    wgs, rng, pmax = _decode_plan([302, 304, 305, 1001], 4)
+    ctxs, T = ([302, 304, 305, 1001], 2) if fmt == "f16" else ([305, 1001], 5)
+    wgs, rng, pmax = _decode_plan(ctxs, 4)
     tiles, f, h, rows = _chunk_plan(17, 4, 6)
     slots = wgs * pmax
     align = lambda x: -(-x // 256) * 256
-    o = align(slots * 12 * 128 * 4)
-    ml = align(slots * 12 * 8)
+    o = align(slots * T * 6 * 128 * 4)
+    ml = align(slots * T * 6 * 8)
     cho = align(tiles * f * h * rows * 128 * 4) if f > 1 else 0
     chml = align(tiles * f * h * rows * 8) if f > 1 else 0
-    dirs = align(4 * 4 * 16)
+    dirs = align(len(ctxs) * 4 * 16)
     assert n == o + ml + cho + chml + dirs
 
 

@@ -37,8 +37,9 @@ CASES = {
     "g1_d64_p48": ("tiny_mixed", 8, dict(hq=2, hkv=2, ps=48)),
     "small_f16": ("small_mixed", 9, dict(kf="f16", vf="f16")),
     "tiny_f16_p48": ("tiny_mixed", 10, dict(kf="f16", vf="f16", ps=48)),
-    # verify rows (2-16 tokens) run on the decode path in groups of 16/G rows;
-    # 17 rows is the shortest prefill chunk
+    # verify rows (2-16 tokens) run on the decode path in sub-rows of 16/G
+    # rows (of 32/G rows over quantized pools when the sequence has more than
+    # 16/G rows); 17 rows is the shortest prefill chunk
     "verify_g6": ("small_mixed", 11, dict(seqs=[(300, 2), (1000, 4), (5, 16), (0, 3), (77, 1), (2000, 7),
                                                  (64, 17)])),
     "verify_g1_p48": ("tiny_mixed", 12, dict(hq=2, hkv=2, ps=48, seqs=[(100, 16), (31, 5), (0, 2), (500, 1),
@@ -46,6 +47,14 @@ CASES = {
     "verify_g8_k4v4": ("tiny_mixed", 13, dict(hq=8, hkv=1, kf="q4", vf="q4", seqs=[(200, 9), (40, 2), (1, 1),
                                                                                       (0, 16)])),
     "verify_f16": ("small_mixed", 14, dict(kf="f16", vf="f16", seqs=[(129, 5), (0, 2), (640, 16), (33, 1)])),
+    # over quantized pools a sequence with more than 16/G rows takes sub-rows
+    # of 32/G rows (two slot groups per wave, stages loaded straight into
+    # LDS run by run): G = 4 on 16-key pages (every stage spans two pages),
+    # D = 64, K8V4; and G = 2 at D = 128 on 48-key pages, K4V8
+    "verify_g4_p16_k8v4": ("tiny_mixed", 15, dict(hq=8, hkv=2, ps=16, kf="q8", vf="q4",
+                                                  seqs=[(100, 16), (31, 5), (0, 7), (250, 9), (3, 1), (60, 4)])),
+    "verify_g2_d128_p48_k4v8": ("tiny_mixed", 16, dict(hq=4, hkv=2, d=128, ps=48, kf="q4", vf="q8",
+                                                       seqs=[(700, 16), (47, 9), (0, 12), (95, 8), (1, 1)])),
 }
 
 
