@@ -201,6 +201,21 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
                             float sm_scale, float* out,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mixed_attention_fwd_timed: mixed_attention_fwd (same operation, arguments,
+ * results and errors) that also times its attention kernel, for measurement:
+ * kernel_start and kernel_stop are hipEvent_t handles (created by the caller,
+ * on the stream's device), recorded on `stream` right before the attention
+ * kernel's launch and right after it, before the merge kernels of the same
+ * call, so that hipEventElapsedTime(kernel_start, kernel_stop) is that
+ * kernel's duration (plus the event records' own few microseconds).  Either
+ * handle may be NULL (not recorded).  A call that returns an error before
+ * enqueueing anything records neither. */
+int32_t mixed_attention_fwd_timed(const mab_kv_layout* layout, const mab_batch* batch,
+                                  const void* q, const void* k_pool, const void* v_pool,
+                                  float sm_scale, float* out,
+                                  void* workspace, int64_t workspace_bytes, void* stream,
+                                  void* kernel_start, void* kernel_stop);
+
 /* mixed_attention_fwd_noalloc: mixed_attention_fwd for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same operation, arguments, results and

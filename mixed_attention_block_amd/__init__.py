@@ -79,6 +79,8 @@ def _lib():
         lib.kv_append_quant.restype = i32
         lib.mixed_attention_fwd.argtypes = [lay, bat, P, P, P, f32, P, P, i64, P]
         lib.mixed_attention_fwd.restype = i32
+        lib.mixed_attention_fwd_timed.argtypes = [lay, bat, P, P, P, f32, P, P, i64, P, P, P]
+        lib.mixed_attention_fwd_timed.restype = i32
         lib.mixed_attention_fwd_noalloc.argtypes = [lay, bat, P, P, P, f32, P, P]
         lib.mixed_attention_fwd_noalloc.restype = i32
         lib.mab_status_string.argtypes, lib.mab_status_string.restype = [i32], ctypes.c_char_p
@@ -185,6 +187,29 @@ def mixed_attention_fwd(layout, batch, q, k_pool, v_pool, sm_scale, out, workspa
                                     workspace.numel(), _stream_handle(stream))
     if st:
         raise MabError(st, "mixed_attention_fwd")
+
+
+def mixed_attention_fwd_timed(layout, batch, q, k_pool, v_pool, sm_scale, out, workspace, kernel_start,
+                              kernel_stop, stream=None):
+    """mixed_attention_fwd that also records the torch.cuda.Event pair
+    ``kernel_start``/``kernel_stop`` right before and after its attention
+    kernel (before the merge kernels): their elapsed time is that kernel's."""
+    _check_tensor(q, "float16", "q")
+    _check_tensor(k_pool, "uint8", "k_pool")
+    _check_tensor(v_pool, "uint8", "v_pool")
+    _check_tensor(out, "float32", "out")
+    _check_tensor(workspace, "uint8", "workspace")
+    handles = []
+    for ev in (kernel_start, kernel_stop):
+        if ev.cuda_event == 0:  # torch creates the event lazily, at its first record
+            ev.record(stream)
+        handles.append(ctypes.c_void_p(ev.cuda_event))
+    st = _lib().mixed_attention_fwd_timed(ctypes.byref(layout), ctypes.byref(batch.struct),
+                                          q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                          float(sm_scale), out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream_handle(stream), *handles)
+    if st:
+        raise MabError(st, "mixed_attention_fwd_timed")
 
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # MAB_NOALLOC_SCRATCH_BYTES

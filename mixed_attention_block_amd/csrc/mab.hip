@@ -2242,7 +2242,7 @@ namespace {
 // The common body of mixed_attention_fwd and mixed_attention_fwd_noalloc.
 int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, const void* q, const void* k_pool,
                        const void* v_pool, float sm_scale, float* out, void* workspace, int64_t workspace_bytes,
-                       void* stream, int32_t too_small) {
+                       void* stream, int32_t too_small, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   int st = check_layout(layout);
   if (st) return st;
   HostPlan hp;
@@ -2298,9 +2298,11 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   }
   const int grid = hp.n_chunk_items + hp.dec_wgs;
   const bool dbg = debug_mode();
+  if (ev_start && hipEventRecord(ev_start, hs) != hipSuccess) return MAB_ERR_HIP;
   if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs, dbg);
   else launch_attention_nb<4>(layout, a, grid, hs, dbg);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
+  if (ev_stop && hipEventRecord(ev_stop, hs) != hipSuccess) return MAB_ERR_HIP;
   if (hp.ch_splits) {
     hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * chunk_combine_parts(layout->head_dim)),
                        dim3(kChunkCombineThreads), 0, hs, a, layout->head_dim);
@@ -2357,6 +2359,13 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
                         MAB_ERR_WORKSPACE);
 }
 
+int32_t mixed_attention_fwd_timed(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
+                                  const void* k_pool, const void* v_pool, float sm_scale, float* out,
+                                  void* workspace, int64_t workspace_bytes, void* stream, void* kernel_start,
+                                  void* kernel_stop) {
+  return attention_call(layout, batch, q, k_pool, v_pool, sm_scale, out, workspace, workspace_bytes, stream,
+                        MAB_ERR_WORKSPACE, (hipEvent_t)kernel_start, (hipEvent_t)kernel_stop);
+}
 int32_t mixed_attention_fwd_noalloc(const mab_kv_layout* layout, const mab_batch* batch, const void* q,
                                     const void* k_pool, const void* v_pool, float sm_scale, float* out,
                                     void* stream) {
