@@ -159,6 +159,18 @@ def chunk_flops(case):
     return f
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None where it is not readable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def chunk_only_launch(st, stream, n):
     """The first layer's prefill chunks alone (its sequences of more than 16
     rows, no decode rows) in one mixed_attention_fwd_timed call, n times: the
@@ -227,7 +239,7 @@ def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(done)} of {case.num_seqs} sequences of this workload (shortest first; "
                       f"{rows} rows, {nbytes / 1e6:.1f} MB of KV): encode + fp64 attention, "
                       f"{elapsed:.1f} s",
