@@ -204,12 +204,12 @@ int32_t mixed_attention_fwd(const mab_kv_layout* layout, const mab_batch* batch,
 /* mixed_attention_fwd_timed: mixed_attention_fwd (same operation, arguments,
  * results and errors) that also times its attention kernel, for measurement:
  * kernel_start and kernel_stop are hipEvent_t handles (created by the caller,
- * on the stream's device), recorded on `stream` right before the attention
- * kernel's launch and right after it, before the merge kernels of the same
- * call, so that hipEventElapsedTime(kernel_start, kernel_stop) is that
- * kernel's duration (plus the event records' own few microseconds).  Either
- * handle may be NULL (not recorded).  A call that returns an error before
- * enqueueing anything records neither. */
+ * on the stream's device) that take the attention kernel's own start and end
+ * timestamps (the kernel is launched through hipExtLaunchKernel), so that
+ * hipEventElapsedTime(kernel_start, kernel_stop) is that kernel's execution
+ * time, without the merge kernels of the same call.  Either handle may be
+ * NULL (not recorded).  A call that returns an error before enqueueing
+ * anything records neither. */
 int32_t mixed_attention_fwd_timed(const mab_kv_layout* layout, const mab_batch* batch,
                                   const void* q, const void* k_pool, const void* v_pool,
                                   float sm_scale, float* out,

@@ -17,6 +17,7 @@
 // bytes; chunk tiles dequantize each 32-key step once into a shared LDS tile
 // and run 16x16x32 MFMAs.  Quantized keys enter the MFMA as exact integer codes
 // with their block scale applied in fp32.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -2154,41 +2155,44 @@ void launch_append(const mab_kv_layout* L, const mab_batch* B, const void* kn, c
 }
 
 template <int NB, int KF, int VF, bool DBG, bool WIDE>
-void launch_attention_build(const AttnArgs& a, int grid, hipStream_t st) {
+// ev0/ev1 (may be null): events that take the kernel's own start and end
+// timestamps (hipExtLaunchKernel), for measurement.
+void launch_attention_build(const AttnArgs& a, int grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kMixedWaves), 0, st,
-                       a);
+    hipExtLaunchKernelGGL((mixed_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kMixedWaves), 0, st,
+                          ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((decode_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kDecodeWaves), 0, st,
-                       a);
+    hipExtLaunchKernelGGL((decode_attention_kernel<NB, KF, VF, DBG, WIDE>), dim3(grid), dim3(64 * kDecodeWaves), 0,
+                          st, ev0, ev1, 0, a);
 }
 
 template <int NB, int KF, int VF, bool DBG>
-void launch_attention_dbg(const AttnArgs& a, int grid, hipStream_t st) {
+void launch_attention_dbg(const AttnArgs& a, int grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if constexpr (DecLayout<NB, KF, VF>::kWideOk) {
     if (a.dec_wide) {
-      launch_attention_build<NB, KF, VF, DBG, true>(a, grid, st);
+      launch_attention_build<NB, KF, VF, DBG, true>(a, grid, st, ev0, ev1);
       return;
     }
   }
-  launch_attention_build<NB, KF, VF, DBG, false>(a, grid, st);
+  launch_attention_build<NB, KF, VF, DBG, false>(a, grid, st, ev0, ev1);
 }
 
 // Debug mode takes instantiations of their own: the page-id checks stay out
 // of the normal kernels' code.
 template <int NB, int KF, int VF>
-void launch_attention(const AttnArgs& a, int grid, hipStream_t st, bool debug) {
-  if (debug) launch_attention_dbg<NB, KF, VF, true>(a, grid, st);
-  else launch_attention_dbg<NB, KF, VF, false>(a, grid, st);
+void launch_attention(const AttnArgs& a, int grid, hipStream_t st, bool debug, hipEvent_t ev0, hipEvent_t ev1) {
+  if (debug) launch_attention_dbg<NB, KF, VF, true>(a, grid, st, ev0, ev1);
+  else launch_attention_dbg<NB, KF, VF, false>(a, grid, st, ev0, ev1);
 }
 
 template <int NB>
-void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st, bool dbg) {
-  if (L->k_format == MAB_KV_F16) launch_attention<NB, MAB_KV_F16, MAB_KV_F16>(a, grid, st, dbg);
-  else if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st, dbg);
-  else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st, dbg);
-  else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st, dbg);
-  else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st, dbg);
+void launch_attention_nb(const mab_kv_layout* L, const AttnArgs& a, int grid, hipStream_t st, bool dbg,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  if (L->k_format == MAB_KV_F16) launch_attention<NB, MAB_KV_F16, MAB_KV_F16>(a, grid, st, dbg, ev0, ev1);
+  else if (L->k_format == MAB_KV_Q8 && L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q8>(a, grid, st, dbg, ev0, ev1);
+  else if (L->k_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q8, MAB_KV_Q4>(a, grid, st, dbg, ev0, ev1);
+  else if (L->v_format == MAB_KV_Q8) launch_attention<NB, MAB_KV_Q4, MAB_KV_Q8>(a, grid, st, dbg, ev0, ev1);
+  else launch_attention<NB, MAB_KV_Q4, MAB_KV_Q4>(a, grid, st, dbg, ev0, ev1);
 }
 
 }  // namespace
@@ -2298,11 +2302,9 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   }
   const int grid = hp.n_chunk_items + hp.dec_wgs;
   const bool dbg = debug_mode();
-  if (ev_start && hipEventRecord(ev_start, hs) != hipSuccess) return MAB_ERR_HIP;
-  if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs, dbg);
-  else launch_attention_nb<4>(layout, a, grid, hs, dbg);
+  if (layout->head_dim == 64) launch_attention_nb<2>(layout, a, grid, hs, dbg, ev_start, ev_stop);
+  else launch_attention_nb<4>(layout, a, grid, hs, dbg, ev_start, ev_stop);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
-  if (ev_stop && hipEventRecord(ev_stop, hs) != hipSuccess) return MAB_ERR_HIP;
   if (hp.ch_splits) {
     hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * chunk_combine_parts(layout->head_dim)),
                        dim3(kChunkCombineThreads), 0, hs, a, layout->head_dim);
