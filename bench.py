@@ -202,8 +202,10 @@ def chunk_only_launch(st, stream, n):
 
 def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
     """The oracle on whole sequences of the case, shortest first, until the
-    budget is spent; a sequence whose predicted time (from the rate so far per
-    row-key pair and per key) would take the total past cap_s is not started."""
+    budget is spent.  A sequence whose predicted time (from the rate so far per
+    row-key pair and per key) would take the total past cap_s is not started
+    whole: its first rows are run instead, as many as the budget left allows
+    (at least one), and its KV bytes are counted in proportion to them."""
     import torch
     from threadpoolctl import threadpool_info
 
@@ -215,15 +217,24 @@ def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
     kp = ocache.new_pool(lay, lay["k_format"])
     vp = ocache.new_pool(lay, lay["v_format"])
     order = sorted(range(case.num_seqs), key=lambda s: case.context(s))  # short first
-    done, nbytes, rows, elapsed, work = [], 0, 0, 0.0, 0.0
+    done, nbytes, rows, elapsed, work = [], 0.0, 0, 0.0, 0.0
+    part = None  # (sequence, rows run of its rows) of a sequence run in part
+    flops = 0
     for s in order:
         r0, r1 = int(case.q_start[s]), int(case.q_start[s + 1])
-        w = (r1 - r0 + 1) * float(case.context(s))  # attention pairs plus the keys encoded
+        ctx = float(case.context(s))
+        w = (r1 - r0 + 1) * ctx  # attention pairs plus the keys encoded
         if done and elapsed + elapsed / work * w > cap_s:
-            break
+            rate = elapsed / work
+            n_rows = int(max(1, min(r1 - r0, (budget_s - elapsed) / (rate * ctx) - 1)))
+            if n_rows >= r1 - r0:
+                break
+            part = (s, n_rows)
+            r1 = r0 + n_rows
+            w = (n_rows + 1) * ctx
         work += w
-        k = torch.cat([case.k_prefix[s].cpu(), case.k_new[r0:r1].cpu()]).numpy()
-        v = torch.cat([case.v_prefix[s].cpu(), case.v_new[r0:r1].cpu()]).numpy()
+        k = torch.cat([case.k_prefix[s].cpu(), case.k_new[int(case.q_start[s]):int(case.q_start[s + 1])].cpu()]).numpy()
+        v = torch.cat([case.v_prefix[s].cpu(), case.v_new[int(case.q_start[s]):int(case.q_start[s + 1])].cpu()]).numpy()
         q = case.q.cpu().numpy()
         t0 = time.perf_counter()
         pos = np.arange(case.context(s))
@@ -233,17 +244,26 @@ def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
                         case.sm_scale, rows=list(range(r0, r1)))
         elapsed += time.perf_counter() - t0
         done.append(s)
-        nbytes += case.context(s) * bpp
+        n_seq = int(case.q_start[s + 1]) - int(case.q_start[s])
+        nbytes += ctx * bpp * (r1 - r0) / n_seq
         rows += r1 - r0
-        if elapsed >= budget_s:
+        if n_seq > 16:  # a prefill chunk: its QK^T and PV flops over the visible keys of the rows run
+            p = int(case.prefix_len[s])
+            flops += sum(4 * lay["head_dim"] * lay["num_q_heads"] * (p + 1 + i) for i in range(r1 - r0))
+        if part is not None or elapsed >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
-            "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": f"{len(done)} of {case.num_seqs} sequences of this workload (shortest first; "
-                      f"{rows} rows, {nbytes / 1e6:.1f} MB of KV): encode + fp64 attention, "
-                      f"{elapsed:.1f} s",
-            "query_tok_s": round(rows / elapsed, 3)}
+    whole = len(done) - (1 if part else 0)
+    sample = (f"{whole} of {case.num_seqs} sequences of this workload whole (shortest first)"
+              + (f" and the first {part[1]} of the {int(case.q_start[part[0] + 1] - case.q_start[part[0]])} rows "
+                 f"of the next" if part else "")
+              + f"; {rows} rows, {nbytes / 1e6:.1f} MB of KV: encode + fp64 attention, {elapsed:.1f} s")
+    out = {"value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+           "cpu_model": cpu_model(), "kind": "oracle", "sample": sample,
+           "query_tok_s": round(rows / elapsed, 3)}
+    if flops:
+        out["chunk_gflops"] = round(flops / elapsed / 1e9, 3)
+    return out
 
 
 # ---- HBM traffic from hardware counters ---------------------------------------
