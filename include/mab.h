@@ -116,8 +116,8 @@ typedef struct mab_kv_layout {
  * own wave.  Prefill-chunk rows are batch-independent either way: their key
  * splits depend only on their own tile count and the device's compute-unit
  * count.  The grouping of a verify row's tokens depends only on its own
- * length and the layout.  Cost on one MI355X: about +30% on a batch of 16
- * short decode rows, +15% on 4-token verify rows, nothing on single long
+ * length and the layout.  Cost on one MI355X: about +26% on a batch of 16
+ * short decode rows, +25% on 4-token verify rows, nothing on single long
  * rows. */
 enum { MAB_BATCH_INVARIANT = 1 };
 #define MAB_INVARIANT_PIECE_KEYS 512
