@@ -229,3 +229,13 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(mab, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="missing"):
         mab.kv_block_bytes("q8")
+
+
+def test_sequence_count_limit():
+    """4096 sequences per batch (the launch-table limit) are accepted; one
+    more is refused as unsupported before anything is enqueued."""
+    lay = mab.make_layout(24, 4, 128, 256, 100)
+    for n, ok in ((4096, True), (4097, False)):
+        q_start = np.arange(n + 1, dtype=np.int32)  # one decode row each
+        ws = _ws(lay, _HostBatch(q_start, np.full(n, 7, np.int32), 1))
+        assert (ws > 0) if ok else ws == -3, (n, ws)
