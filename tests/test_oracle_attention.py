@@ -207,3 +207,13 @@ def test_row_sampling_matches_full():
     part = run_oracle(case, kp, vp, rows=rows)
     assert np.array_equal(part[rows], full[rows])
     assert np.isnan(part[1]).all()
+
+
+def test_pool_size_closed_form():
+    # pages x KV heads x page slots x blocks per token x block bytes (the pool
+    # layout of the paged cache; 34/18/64-byte blocks from the modes table)
+    for fmt, bb in (("q8", 34), ("q4", 18), ("f16", 64)):
+        lay = dict(num_q_heads=24, num_kv_heads=4, head_dim=128, page_size=256, num_pages=7)
+        assert cache.pool_shape(lay, fmt) == (7, 4, 256, 4, bb)
+        assert cache.pool_bytes(lay, fmt) == 7 * 4 * 256 * 4 * bb
+        assert cache.new_pool(lay, fmt).nbytes == cache.pool_bytes(lay, fmt)
