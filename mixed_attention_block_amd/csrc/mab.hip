@@ -712,11 +712,15 @@ __device__ inline void dec_compute(Group<NB> (&gr)[NG], const uint8_t* raw, cons
         for (int i = 0; i < 4; ++i)
           if (kbase + 16 * kt + 4 * j + i >= min(kend, g.limit + 1)) s[k][kt][i] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
-                     fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3])));
-    mx = max_xor32(max_xor16(mx));
-    const bool grow = mx > g.m + (big_v ? 0.f : kRescaleSlack);  // also true for the first keys (m = -inf)
-    if (__any(grow)) {
+    // the slot's max grows past the threshold only if one of its lanes' values
+    // does: the lane-swap reduction runs only then (rarely after the first
+    // stages)
+    const float lmx = fmaxf(fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
+                            fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3])));
+    const float thr = g.m + (big_v ? 0.f : kRescaleSlack);  // -inf for the first keys (m = -inf)
+    if (__any(lmx > thr)) {
+      const float mx = max_xor32(max_xor16(lmx));
+      const bool grow = mx > thr;
       const float m_new = grow ? mx : g.m;
       const float alpha = grow ? __builtin_amdgcn_exp2f(g.m - m_new) : 1.f;  // 0 when m was -inf
 #pragma unroll
