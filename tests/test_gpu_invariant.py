@@ -35,8 +35,8 @@ def _inv_batch(case):
 
 
 @pytest.mark.parametrize("kf,vf,hq,hkv,ps", [("q8", "q8", 24, 4, 32), ("q4", "q4", 24, 4, 64),
-                                             ("q8", "q4", 8, 1, 48)],
-                         ids=["q8_g6_p32", "k4v4_g6_p64", "k8v4_g8_p48"])
+                                             ("q8", "q4", 8, 1, 48), ("q4", "q8", 14, 2, 16)],
+                         ids=["q8_g6_p32", "k4v4_g6_p64", "k8v4_g8_p48", "k4v8_g7_p16"])
 def test_invariant_matches_oracle(kf, vf, hq, hkv, ps):
     case = synth.make_case("small_mixed", 71, device="cuda", seqs=SEQS, kf=kf, vf=vf, hq=hq, hkv=hkv, ps=ps)
     _say(f"invariant vs oracle {kf}/{vf} hq={hq} hkv={hkv} ps={ps}")

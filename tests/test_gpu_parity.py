@@ -55,6 +55,21 @@ CASES = {
                                                   seqs=[(100, 16), (31, 5), (0, 7), (250, 9), (3, 1), (60, 4)])),
     "verify_g2_d128_p48_k4v8": ("tiny_mixed", 16, dict(hq=4, hkv=2, d=128, ps=48, kf="q4", vf="q8",
                                                        seqs=[(700, 16), (47, 9), (0, 12), (95, 8), (1, 1)])),
+    # odd groups above 1 leave MFMA slots idle: sub-rows of 16/G rows (5 at
+    # G = 3, 3 at G = 5, 2 at G = 7) or 32/G over quantized pools (10, 6, 4),
+    # and chunk tiles of one head (256 rows); row counts on both sides of
+    # each sub-row size
+    "g3_d128_p32_k4v4": ("tiny_mixed", 17, dict(hq=6, hkv=2, d=128, ps=32, kf="q4", vf="q4",
+                                                seqs=[(100, 40), (300, 5), (64, 6), (0, 10), (777, 11), (5, 1),
+                                                      (1500, 16)])),
+    "g5_d64_p16_q8": ("tiny_mixed", 18, dict(hq=10, hkv=2, ps=16,
+                                             seqs=[(200, 16), (50, 3), (0, 25), (10, 1), (333, 4), (77, 6),
+                                                   (90, 7)])),
+    "g7_d128_p48_k8v4": ("tiny_mixed", 19, dict(hq=14, hkv=2, d=128, ps=48, kf="q8", vf="q4",
+                                                seqs=[(300, 2), (40, 16), (0, 17), (129, 1), (1000, 3), (61, 4),
+                                                      (7, 5)])),
+    "g7_d64_p64_f16": ("tiny_mixed", 20, dict(hq=7, hkv=1, ps=64, kf="f16", vf="f16",
+                                              seqs=[(100, 9), (33, 1), (0, 20), (250, 2), (64, 3)])),
 }
 
 
@@ -109,7 +124,7 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("key", ["tiny_mixed", "small_q8", "verify_g6"])
+@pytest.mark.parametrize("key", ["tiny_mixed", "small_q8", "verify_g6", "g5_d64_p16_q8"])
 def test_mixed_equals_separate(key):
     """One mixed launch versus launches of its parts.  Chunk rows are computed
     by work items that depend only on their own sequence: bitwise equal.  Decode
