@@ -200,6 +200,73 @@ def chunk_only_launch(st, stream, n):
             "note": "the first layer's prefill chunk alone (no decode rows), attention kernel only"}
 
 
+def decode_sweep(n=30):
+    """Decode-only batches of growing size: 16 and 64 rows with decode16's
+    heads (24/4, head_dim 128, page 256) and contexts uniform in
+    [1024*m, 32768*m] (capped at 262144) for m = 1, 2, 4, 8, over q8 and K4V4
+    pools.  Per point: the attention kernel's average duration over n timed
+    calls (the library's event pair around its launch), the whole call's
+    (back-to-back calls), and the KV bytes each moves per launch.  One JSON
+    line per point, then a fit of kernel time = fixed + bytes / rate."""
+    import torch
+    import mixed_attention_block_amd as mab
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    pts = []
+    for kf, vf in (("q8", "q8"), ("q4", "q4")):
+        for rows in (16, 64):
+            for m in (1, 2, 4, 8):
+                rng = np.random.Generator(np.random.PCG64(1000 * rows + m))
+                ctx = np.minimum(rng.integers(1024 * m, 32768 * m, size=rows, endpoint=True), 262144)
+                case = synth.make_case("decode16", 2, device="cuda", seqs=[(int(c) - 1, 1) for c in ctx],
+                                       kf=kf, vf=vf, outliers=0.02)
+                st = DeviceCase(case)
+                case.k_prefix = case.v_prefix = None
+                kv = int(ctx.sum()) * kv_bytes_per_position(case.layout)
+                # identical pool copies rotated, as in the timed steps, so that
+                # repeated calls do not find a small batch in the Infinity Cache
+                copies = max(1, min(16, math.ceil((1 << 30) / (st.k_pool.numel() + st.v_pool.numel()))))
+                pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
+                                                    for _ in range(copies - 1)]
+                call = lambda i: mab.mixed_attention_fwd(st.layout, st.batch, st.q, *pools[i % copies],
+                                                         case.sm_scale, st.out, st.ws, stream)
+                for i in range(3):
+                    call(i)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(n):
+                    call(i)
+                e1.record(stream)
+                kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(n)]
+                for i, (a, b) in enumerate(kev):
+                    mab.mixed_attention_fwd_timed(st.layout, st.batch, st.q, *pools[i % copies], case.sm_scale,
+                                                  st.out, st.ws, a, b, stream)
+                torch.cuda.synchronize()
+                call_us = e0.elapsed_time(e1) / n * 1e3
+                kern_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
+                pt = {"format": f"K{kf}/V{vf}", "rows": rows, "ctx_scale": m, "kv_bytes": kv, "pool_copies": copies,
+                      "kernel_us": round(kern_us, 2), "call_us": round(call_us, 2),
+                      "kernel_tbs": round(kv / kern_us / 1e6, 3),
+                      "kernel_frac": round(kv / kern_us / 1e6 / (HBM_PEAK_GBS / 1e3), 4),
+                      "call_frac": round(kv / call_us / 1e6 / (HBM_PEAK_GBS / 1e3), 4)}
+                print(json.dumps(pt), flush=True)
+                pts.append(pt)
+                del st, case, pools, call
+                torch.cuda.empty_cache()
+    for fmt in ("Kq8/Vq8", "Kq4/Vq4"):
+        p = [q for q in pts if q["format"] == fmt]
+        x = np.array([q["kv_bytes"] for q in p], np.float64)
+        y = np.array([q["kernel_us"] for q in p], np.float64)
+        slope, icpt = np.polyfit(x, y, 1)
+        print(json.dumps({"format": fmt, "fit": "kernel_us = fixed_us + kv_bytes / rate",
+                          "fixed_us": round(float(icpt), 2), "rate_tbs": round(1 / float(slope) / 1e6, 3)}),
+              flush=True)
+
+
 def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
     """The oracle on whole sequences of the case, shortest first, until the
     budget is spent.  A sequence whose predicted time (from the rate so far per
@@ -396,6 +463,9 @@ def ingest_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 def main():
     if "--copy-probe" in sys.argv:
         copy_probe()
+        return
+    if "--decode-sweep" in sys.argv:
+        decode_sweep()
         return
     if "--ingest-pmc" in sys.argv:
         ap = argparse.ArgumentParser()
