@@ -267,6 +267,55 @@ def decode_sweep(n=30):
               flush=True)
 
 
+def chunk_sweep(n=10):
+    """Prefill-chunk-only batches: one sequence of C new rows after a cached
+    prefix of P tokens (C = 512, 2048, 4096; P = 8192, 32768, 131072) with
+    24/4 heads, head_dim 128, page 256, K outliers, over q8 and K4V4 pools.
+    Per point: the attention kernel's average duration over n timed calls and
+    its fraction of the 2.5 PFLOP/s fp16 peak over the chunk's visible
+    (row, key) pairs, and the whole call's.  One JSON line per point."""
+    import torch
+    import mixed_attention_block_amd as mab
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    for kf, vf in (("q8", "q8"), ("q4", "q4")):
+        for prefix in (8192, 32768, 131072):
+            for rows in (512, 2048, 4096):
+                case = synth.make_case("mixed16_chunk2k", 3, device="cuda", seqs=[(prefix, rows)], kf=kf, vf=vf)
+                st = DeviceCase(case)
+                case.k_prefix = case.v_prefix = None
+                flops = chunk_flops(case)
+                call = lambda: mab.mixed_attention_fwd(st.layout, st.batch, st.q, st.k_pool, st.v_pool,
+                                                       case.sm_scale, st.out, st.ws, stream)
+                for _ in range(2):
+                    call()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    call()
+                e1.record(stream)
+                kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(n)]
+                for a, b in kev:
+                    mab.mixed_attention_fwd_timed(st.layout, st.batch, st.q, st.k_pool, st.v_pool, case.sm_scale,
+                                                  st.out, st.ws, a, b, stream)
+                torch.cuda.synchronize()
+                call_ms = e0.elapsed_time(e1) / n
+                kern_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+                tf = flops / (kern_ms * 1e-3) / 1e12
+                print(json.dumps({"format": f"K{kf}/V{vf}", "prefix": prefix, "rows": rows, "flops": int(flops),
+                                  "kernel_ms": round(kern_ms, 4), "call_ms": round(call_ms, 4),
+                                  "kernel_tflops": round(tf, 1),
+                                  "kernel_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                  "call_frac": round(flops / (call_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}),
+                      flush=True)
+                del st, case, call
+                torch.cuda.empty_cache()
+
+
 def cpu_baseline(case, budget_s=12.0, cap_s=30.0):
     """The oracle on whole sequences of the case, shortest first, until the
     budget is spent.  A sequence whose predicted time (from the rate so far per
@@ -466,6 +515,9 @@ def main():
         return
     if "--decode-sweep" in sys.argv:
         decode_sweep()
+        return
+    if "--chunk-sweep" in sys.argv:
+        chunk_sweep()
         return
     if "--ingest-pmc" in sys.argv:
         ap = argparse.ArgumentParser()
