@@ -150,13 +150,17 @@ __host__ __device__ inline int dec_subrows(int q_len, int group, bool wide) {
 __host__ __device__ inline int chunk_tiles(int q_len, int hkv, int group) {
   return ceil_div(q_len, chunk_rows(group)) * hkv * (group / chunk_heads(group));
 }
-// Tile t of a chunk sequence with n_qt row tiles and n_hp head groups: row
-// tile qt, head group hp, KV head g.  Row tiles run last first: a later row
-// tile sees more keys, and work items start in grid order as work-groups
-// free, so the longest items start first and the last to start are short.
+// Tile t of a chunk sequence with n_qt row tiles, n_hp head groups and hkv
+// KV heads: row tile qt, head group hp, KV head g.  The row tile varies
+// slowest and runs last first: a later row tile sees more keys, and work
+// items start in grid order as work-groups free, so the longest items start
+// first and the last to start are short; the items of one row tile (all
+// head groups and KV heads, equally long) are consecutive, so work-groups
+// dealt round-robin over the XCDs get equal shares.
 struct ChunkTileCoord { int qt, hp, g; };
-__host__ __device__ inline ChunkTileCoord chunk_tile_coord(int t, int n_qt, int n_hp) {
-  return ChunkTileCoord{n_qt - 1 - t % n_qt, (t / n_qt) % n_hp, t / (n_qt * n_hp)};
+__host__ __device__ inline ChunkTileCoord chunk_tile_coord(int t, int n_qt, int n_hp, int hkv) {
+  const int c = t % (n_hp * hkv);
+  return ChunkTileCoord{n_qt - 1 - t / (n_hp * hkv), c % n_hp, c / n_hp};
 }
 __host__ __device__ inline int dec_stages(int ctx) { return ceil_div(ctx, kStepKeys); }
 // Units a decode segment takes in the decode stream: its stages, or, for
@@ -1702,7 +1706,7 @@ __device__ inline void chunk_work(const AttnArgs& a, uint8_t* smem, int item) {
   const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
   const int n_qt = ceil_div(q_len, R), n_hp = G / H;
   const int tile = local / F, j = local % F;
-  const ChunkTileCoord tc = chunk_tile_coord(tile, n_qt, n_hp);
+  const ChunkTileCoord tc = chunk_tile_coord(tile, n_qt, n_hp, a.hkv);
   const int qt = tc.qt, hp = tc.hp, g = tc.g;
   ItemCtx ic;
   ic.k_pool = a.k_pool;
@@ -1873,7 +1877,7 @@ chunk_combine_kernel(AttnArgs a, int head_dim) {
   const int r0 = tv.ch_r0[c], q_len = tv.ch_qlen[c];
   const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
   const int n_qt = ceil_div(q_len, R), n_hp = G / H;
-  const ChunkTileCoord tc = chunk_tile_coord(local / F, n_qt, n_hp);
+  const ChunkTileCoord tc = chunk_tile_coord(local / F, n_qt, n_hp, a.hkv);
   const int qt = tc.qt, hp = tc.hp, g = tc.g;
   const int tpr = head_dim / 4;                           // threads per row
   const int rt = part * (kChunkCombineThreads / tpr) + threadIdx.x / tpr;  // row of the tile, head-major
