@@ -1856,54 +1856,59 @@ combine_kernel(AttnArgs a) {
 }
 
 // Merges the key splits of chunk tiles cut into more than one split.  A tile
-// holds H*R = 32*kMixedWaves rows (all its heads); work-group (item, part)
-// merges rows [part*RB, (part+1)*RB) of the tile if item is the tile's split 0
-// (the others exit at once): thread (row, 4 dims) takes the global max of the
-// splits' maxima, then sums the weighted partials in split order, with every
-// split's loads in flight together.  Deterministic.
+// holds H*R = 32*kMixedWaves rows (all its heads); its F split items each
+// own kChunkCombineGroups work-groups, and work-group q of split j merges
+// the tile's rows [(j*kChunkCombineGroups + q)*per, ...+per), per =
+// ceil(H*R / (F*kChunkCombineGroups)), so no work-group is idle: thread
+// (row, 4 dims) takes the global max of the splits' maxima, then sums the
+// weighted partials in split order, with every split's loads in flight
+// together.  Deterministic.
 constexpr int kChunkCombineThreads = 256;
-__host__ __device__ inline int chunk_combine_parts(int head_dim) {
-  return 32 * kMixedWaves / (kChunkCombineThreads / (head_dim / 4));
-}
+constexpr int kChunkCombineGroups = 8;  // work-groups per split item
 
 __global__ void __launch_bounds__(kChunkCombineThreads)
 chunk_combine_kernel(AttnArgs a, int head_dim) {
   const TabView tv = tab_view(a);
-  const int parts = chunk_combine_parts(head_dim);
-  const int item = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int item = blockIdx.x / kChunkCombineGroups, q = blockIdx.x % kChunkCombineGroups;
   const int c = wave_find(tv.ch_item, a.n_chunk, item);
   const int local = item - tv.ch_item[c], F = tv.ch_split[c];
-  if (F == 1 || local % F != 0) return;
+  if (F == 1) return;
+  const int j = local % F, first = item - j;  // the tile's split 0
   const int r0 = tv.ch_r0[c], q_len = tv.ch_qlen[c];
   const int G = a.hq / a.hkv, H = chunk_heads(G), R = chunk_rows(G);
   const int n_qt = ceil_div(q_len, R), n_hp = G / H;
   const ChunkTileCoord tc = chunk_tile_coord(local / F, n_qt, n_hp, a.hkv);
   const int qt = tc.qt, hp = tc.hp, g = tc.g;
   const int tpr = head_dim / 4;                           // threads per row
-  const int rt = part * (kChunkCombineThreads / tpr) + threadIdx.x / tpr;  // row of the tile, head-major
-  const int hh = rt / R, rr = rt % R, dd = 4 * (threadIdx.x % tpr);
-  const int i = qt * R + rr;
-  if (i >= q_len) return;
-  float2 ml[kMaxChunkSplit];
-  float mx = -INFINITY;
+  const int rpp = kChunkCombineThreads / tpr;             // rows per pass
+  const int per = ceil_div(H * R, F * kChunkCombineGroups);
+  const int lo = (j * kChunkCombineGroups + q) * per, hi = min(H * R, lo + per);
+  const int dd = 4 * (threadIdx.x % tpr);
+  for (int rt = lo + threadIdx.x / tpr; rt < hi; rt += rpp) {  // row of the tile, head-major
+    const int hh = rt / R, rr = rt % R;
+    const int i = qt * R + rr;
+    if (i >= q_len) continue;
+    float2 ml[kMaxChunkSplit];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kMaxChunkSplit; ++j) {
-    ml[j] = make_float2(-INFINITY, 0.f);
-    if (j < F) ml[j] = a.ch_ml[((int64_t)(item + j) * H + hh) * R + rr];
-    mx = fmaxf(mx, ml[j].x);
-  }
-  float l = 0.f;
-  float4_t o = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kMaxChunkSplit; ++j) {
-    if (j < F && ml[j].y > 0.f) {  // an empty split (no keys) has l = 0 and unwritten o
-      const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
-      const int64_t pi = ((int64_t)(item + j) * H + hh) * R + rr;
-      l += w * ml[j].y;
-      o += w * *reinterpret_cast<const float4_t*>(a.ch_o + pi * head_dim + dd);
+    for (int jj = 0; jj < kMaxChunkSplit; ++jj) {
+      ml[jj] = make_float2(-INFINITY, 0.f);
+      if (jj < F) ml[jj] = a.ch_ml[((int64_t)(first + jj) * H + hh) * R + rr];
+      mx = fmaxf(mx, ml[jj].x);
     }
+    float l = 0.f;
+    float4_t o = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < kMaxChunkSplit; ++jj) {
+      if (jj < F && ml[jj].y > 0.f) {  // an empty split (no keys) has l = 0 and unwritten o
+        const float w = __builtin_amdgcn_exp2f(ml[jj].x - mx);
+        const int64_t pi = ((int64_t)(first + jj) * H + hh) * R + rr;
+        l += w * ml[jj].y;
+        o += w * *reinterpret_cast<const float4_t*>(a.ch_o + pi * head_dim + dd);
+      }
+    }
+    *reinterpret_cast<float4_t*>(a.out + ((int64_t)(r0 + i) * a.hq + g * G + hp * H + hh) * head_dim + dd) = o / l;
   }
-  *reinterpret_cast<float4_t*>(a.out + ((int64_t)(r0 + i) * a.hq + g * G + hp * H + hh) * head_dim + dd) = o / l;
 }
 
 // Writes the launch-order tables to the workspace for batches too large for
@@ -2323,7 +2328,7 @@ int32_t attention_call(const mab_kv_layout* layout, const mab_batch* batch, cons
   else launch_attention_nb<4>(layout, a, grid, hs, dbg, ev_start, ev_stop);
   if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   if (hp.ch_splits) {
-    hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * chunk_combine_parts(layout->head_dim)),
+    hipLaunchKernelGGL(chunk_combine_kernel, dim3(hp.n_chunk_items * kChunkCombineGroups),
                        dim3(kChunkCombineThreads), 0, hs, a, layout->head_dim);
     if (hipGetLastError() != hipSuccess) return MAB_ERR_HIP;
   }
