@@ -151,16 +151,19 @@ __host__ __device__ inline int chunk_tiles(int q_len, int hkv, int group) {
   return ceil_div(q_len, chunk_rows(group)) * hkv * (group / chunk_heads(group));
 }
 // Tile t of a chunk sequence with n_qt row tiles, n_hp head groups and hkv
-// KV heads: row tile qt, head group hp, KV head g.  The row tile varies
-// slowest and runs last first: a later row tile sees more keys, and work
-// items start in grid order as work-groups free, so the longest items start
-// first and the last to start are short; the items of one row tile (all
-// head groups and KV heads, equally long) are consecutive, so work-groups
-// dealt round-robin over the XCDs get equal shares.
+// KV heads: row tile qt, head group hp, KV head g; a tile's F key splits are
+// work items t*F .. t*F+F-1.  The row tile varies slowest and runs last
+// first: a later row tile sees more keys, and work items start in grid order
+// as work-groups free, so the longest items start first and the last to
+// start are short.  The items of one row tile (all head groups, KV heads and
+// splits, equally long) are consecutive, so the work-groups, dealt
+// round-robin over the eight XCDs, give each XCD an equal share; the KV head
+// varies fastest, so an XCD sees the same few (KV head, key split) ranges in
+// every row tile and its items share their K/V bytes in its L2.
 struct ChunkTileCoord { int qt, hp, g; };
 __host__ __device__ inline ChunkTileCoord chunk_tile_coord(int t, int n_qt, int n_hp, int hkv) {
-  const int c = t % (n_hp * hkv);
-  return ChunkTileCoord{n_qt - 1 - t / (n_hp * hkv), c % n_hp, c / n_hp};
+  const int u = t / hkv;
+  return ChunkTileCoord{n_qt - 1 - u / n_hp, u % n_hp, t % hkv};
 }
 __host__ __device__ inline int dec_stages(int ctx) { return ceil_div(ctx, kStepKeys); }
 // Units a decode segment takes in the decode stream: its stages, or, for
