@@ -70,6 +70,13 @@ CASES = {
                                                       (7, 5)])),
     "g7_d64_p64_f16": ("tiny_mixed", 20, dict(hq=7, hkv=1, ps=64, kf="f16", vf="f16",
                                               seqs=[(100, 9), (33, 1), (0, 20), (250, 2), (64, 3)])),
+    # more KV heads than the benchmark shapes: eight (G = 8, 64 query heads)
+    # and sixteen without grouping (G = 1), so that a chunk's work items span
+    # many (KV head, key split) pairs
+    "g8_hkv8_d128_p64_k4v4": ("tiny_mixed", 21, dict(hq=64, hkv=8, d=128, ps=64, kf="q4", vf="q4",
+                                                     seqs=[(300, 70), (1000, 1), (77, 4), (0, 33), (5, 16)])),
+    "g1_hkv16_d64_p32_q8": ("tiny_mixed", 22, dict(hq=16, hkv=16, ps=32,
+                                                   seqs=[(200, 300), (4000, 1), (31, 2), (0, 17), (64, 12)])),
 }
 
 
