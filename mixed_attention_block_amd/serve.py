@@ -19,6 +19,7 @@ GEMMs, one layer, no sampling.
 import argparse
 import json
 import sys
+import time
 
 import numpy as np
 import torch
@@ -58,7 +59,8 @@ def warm_up(loop):
     """One untimed decode step and one untimed 32-row chunk step on page 0, as
     an engine runs before it serves: the library's first launches (code
     object load and set-up) stay out of the first measured tick.  The rows'
-    K/V land in slots that any request using page 0 writes before it reads."""
+    K/V land in slots that any request using page 0 writes before it reads.
+    Then half a second of matrix-core work lets the clock settle."""
     from . import BatchDesc
     hq, hkv, d = loop.layout.num_q_heads, loop.layout.num_kv_heads, loop.layout.head_dim
     for rows in (1, 32):
@@ -73,6 +75,14 @@ def warm_up(loop):
             loop.workspace = torch.empty(need, dtype=torch.uint8, device=loop.device)
         loop.launch(batch, q, kv, kv, out)
     torch.cuda.synchronize()
+    # half a second of matrix-core work, so that the first ticks run at the
+    # sustained clock rather than while it ramps up from the idle set-up
+    from . import mab_probe_mfma_f16
+    sink = torch.zeros(4, dtype=torch.float32, device=loop.device)
+    t = time.time()
+    while time.time() - t < 0.5:
+        mab_probe_mfma_f16(20000, sink)
+        torch.cuda.synchronize()
 
 
 def simulate(loop, arrivals, seed=0, max_ticks=1_000_000):
