@@ -217,8 +217,8 @@ def clock_warmup(stream, seconds=0.5):
 def decode_sweep(n=30):
     """Decode-only batches of growing size: 16 and 64 rows with decode16's
     heads (24/4, head_dim 128, page 256) and contexts uniform in
-    [1024*m, 32768*m] (capped at 262144) for m = 1, 2, 4, 8, over q8 and K4V4
-    pools.  Per point: the attention kernel's average duration over n timed
+    [1024*m, 32768*m] (capped at 262144) for m = 1, 2, 4, 8, over q8, K4V4,
+    K8V4 and K4V8 pools.  Per point: the attention kernel's average duration over n timed
     calls (the library's event pair around its launch), the whole call's
     (back-to-back calls), and the KV bytes each moves per launch.  One JSON
     line per point, then a fit of kernel time = fixed + bytes / rate."""
@@ -230,7 +230,7 @@ def decode_sweep(n=30):
     stream = torch.cuda.current_stream()
     clock_warmup(stream)
     pts = []
-    for kf, vf in (("q8", "q8"), ("q4", "q4")):
+    for kf, vf in (("q8", "q8"), ("q4", "q4"), ("q8", "q4"), ("q4", "q8")):
         for rows in (16, 64):
             for m in (1, 2, 4, 8):
                 rng = np.random.Generator(np.random.PCG64(1000 * rows + m))
@@ -273,7 +273,7 @@ def decode_sweep(n=30):
                 pts.append(pt)
                 del st, case, pools, call
                 torch.cuda.empty_cache()
-    for fmt in ("Kq8/Vq8", "Kq4/Vq4"):
+    for fmt in ("Kq8/Vq8", "Kq4/Vq4", "Kq8/Vq4", "Kq4/Vq8"):
         p = [q for q in pts if q["format"] == fmt]
         x = np.array([q["kv_bytes"] for q in p], np.float64)
         y = np.array([q["kernel_us"] for q in p], np.float64)
@@ -286,7 +286,8 @@ def decode_sweep(n=30):
 def chunk_sweep(n=10):
     """Prefill-chunk-only batches: one sequence of C new rows after a cached
     prefix of P tokens (C = 512, 2048, 4096; P = 8192, 32768, 131072) with
-    24/4 heads, head_dim 128, page 256, K outliers, over q8 and K4V4 pools.
+    24/4 heads, head_dim 128, page 256, K outliers, over q8, K4V4, K8V4 and
+    K4V8 pools.
     Per point: the attention kernel's average duration over n timed calls and
     its fraction of the 2.5 PFLOP/s fp16 peak over the chunk's visible
     (row, key) pairs, and the whole call's.  One JSON line per point."""
@@ -297,7 +298,7 @@ def chunk_sweep(n=10):
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     clock_warmup(stream)
-    for kf, vf in (("q8", "q8"), ("q4", "q4")):
+    for kf, vf in (("q8", "q8"), ("q4", "q4"), ("q8", "q4"), ("q4", "q8")):
         for prefix in (8192, 32768, 131072):
             for rows in (512, 2048, 4096):
                 case = synth.make_case("mixed16_chunk2k", 3, device="cuda", seqs=[(prefix, rows)], kf=kf, vf=vf)
